@@ -1,0 +1,237 @@
+"""Throughput of the forward linear-layer GEMM family on one MI355X.
+
+One step is one forward pass of the fused GEMM family over a 512-token batch
+with the model shape of the pages (d_model 768, d_ff 3072, vocabulary 16384):
+
+  qkvo_residual   matmul_residual            512 x 768  x 768    fp32 W, +R
+  qkvo            matmul                     512 x 768  x 768    fp32 W
+  ffn_down        matmul_residual_swiglu_a   512 x 3072 x 768    fp32 W, +R
+  ffn_gate_up     matmul_w16                 512 x 768  x 3072   f16 W
+  lm_head         matmul_w16                 512 x 768  x 16384  f16 W
+
+so every stage of the path runs in each step (plain and SwiGLU A staging,
+fp32 and binary16 B staging, with and without the residual epilogue).
+Inputs are the seeded synthetic arrays of the parity tests, resident in HBM
+before the timed region.  The value is TFLOP/s = 2*M*N*K summed over the step,
+divided by the wall time per step.  The roofline object describes the
+dominant kernel (lm_head) against the fp32 matrix-core peak of MI355X, with
+its average duration taken from HIP events recorded around each of its
+launches in the timed region.
+
+The CPU baseline is the fp64 oracle, timed on whole steps of the same five
+products (repeated for at least --cpu-seconds), on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # 256 CU x 256 flop/clk/CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "TFLOP/s of fused forward GEMMs (seq 512, d768/3072/16384); % FP32 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "tiled_dense_gemm_matmul_amd", "csrc", "gemm_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload():
+    from tiled_dense_gemm_matmul_amd import inputs
+    c2, c3, c4 = inputs.cfg2(), inputs.cfg3(), inputs.cfg4()
+    return [
+        ("qkvo_residual", {"X": c2["X"], "W": c2["W"], "R": c2["R"]}),
+        ("qkvo", {"X": c2["X"], "W": c2["W"]}),
+        ("ffn_down", {"G": c3["G"], "U": c3["U"], "W": c3["W"], "R": c3["R"]}),
+        ("ffn_gate_up", {"X": c4["X"], "W": c4["W_gu"]}),
+        ("lm_head", {"X": c4["X"], "W": c4["W_lm"]}),
+    ]
+
+
+def shape_of(case):
+    A = case["G"] if "G" in case else case["X"]
+    return A.shape[0], A.shape[1], case["W"].shape[1]
+
+
+def cpu_baseline(cases, min_seconds):
+    """The fp64 oracle on whole steps (every output row of the five
+    products), repeated until at least min_seconds have passed."""
+    import oracle
+    oracle.build(force=False)
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    step_flops = sum(2 * shape_of(c)[0] * shape_of(c)[1] * shape_of(c)[2] for _, c in cases)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for _, c in cases:
+            A = c["G"] if "G" in c else c["X"]
+            oracle.gemm(A, c["W"], R=c.get("R"), U=c.get("U"), threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {
+        "value": reps * step_flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{reps} whole steps (all rows of the 5 products, "
+                  f"{reps * step_flops / 1e9:.1f} GFLOP of fp64) in {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards by rows or columns with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    cases = workload()
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    launches = []
+    for name, c in cases:
+        M, K, N = shape_of(c)
+        W = d(c["W"])
+        R = d(c["R"]) if "R" in c else None
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        w16 = c["W"].dtype == np.float16
+        if "G" in c:
+            G, U = d(c["G"]), d(c["U"])
+            keep = (G, U, W, R, Y)
+            args_ = (G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(), Y.data_ptr(), M, K, N,
+                     binding.GEMM_W_F16 if w16 else binding.GEMM_W_F32)
+            fn = binding.load_library().gemm_fwd_swiglu
+            cfg = binding.kernel_config(M, K, N, swiglu=True, w16=w16)
+        else:
+            X = d(c["X"])
+            keep = (X, W, R, Y)
+            args_ = (X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), Y.data_ptr(), M, K, N,
+                     binding.GEMM_FLAG_W_F16 if w16 else 0)
+            fn = binding.load_library().gemm_fwd
+            cfg = binding.kernel_config(M, K, N, swiglu=False, w16=w16)
+        launches.append({"name": name, "fn": fn, "args": args_, "keep": keep, "M": M, "K": K, "N": N,
+                         "flops": 2 * M * N * K, "w16": w16, "config": cfg,
+                         "bytes": (M * K * (8 if "G" in c else 4) + K * N * (2 if w16 else 4)
+                                   + M * N * 4 * (2 if R is not None else 1))})
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def step(events=None):
+        for i, L in enumerate(launches):
+            if events is not None:
+                events[i][0].record(stream)
+            st = L["fn"](*L["args"], sp)
+            if st != 0:
+                raise RuntimeError(f"{L['name']}: {binding.status_string(st)}")
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_flops = sum(L["flops"] for L in launches)
+    ms_per_step = wall / args.steps * 1e3
+    kernels = {}
+    for i, L in enumerate(launches):
+        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        avg_us = float(np.mean(ms)) * 1e3
+        kernels[L["name"]] = {
+            "M": L["M"], "K": L["K"], "N": L["N"], "w": "f16" if L["w16"] else "f32",
+            "config": L["config"], "avg_us": round(avg_us, 3),
+            "median_us": round(float(np.median(ms)) * 1e3, 3),
+            "tflops": round(L["flops"] / avg_us / 1e6, 3),
+            "frac_fp32_mfma_peak": round(L["flops"] / avg_us / 1e6 / PEAK_FP32_MFMA_TFLOPS, 4),
+            "alg_GBps": round(L["bytes"] / avg_us / 1e3, 1),
+        }
+
+    dom = next(L for L in launches if L["name"] == "lm_head")
+    dk = kernels["lm_head"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_sha256_16") == kernel_hash():
+            traffic = t.get("bytes_per_launch")
+    achieved = dom["flops"] / dk["avg_us"] / 1e6
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
+        "kernel": "lm_head (matmul_w16 512x768x16384)",
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cases, args.cpu_seconds)
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "seq512 forward GEMM family: qkvo_residual + qkvo (512x768x768 f32 W), "
+                        "ffn_down swiglu (512x3072x768 f32 W, +R), ffn_gate_up (512x768x3072 f16 W), "
+                        "lm_head (512x768x16384 f16 W)",
+            "step_gflop": round(step_flops / 1e9, 4),
+            "frac_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,124 @@
+/*
+ * gemm_fwd.h — C ABI of the MI355X (gfx950) forward linear-layer GEMM family.
+ *
+ * The operations are the forward linear kernels of a transformer training
+ * engine, defined on the page "matmul ve matmul_residual — Tiled Matrix
+ * Multiply (Forward)" (https://llm.istanbul/learn/tr/03_linear_forward),
+ * section "Ne Yapar?":
+ *
+ *   matmul                        Y = X @ W
+ *   matmul_residual               Y = X @ W + R           (R added after the sum)
+ *   matmul_residual_swiglu_a      Y = (silu(GATE) * UP) @ W + R
+ *   *_w16                         the same with IEEE binary16 weights
+ *
+ * with silu(x) = x * sigmoid(x) and the sign-branched sigmoid of the page
+ * "ffn_gelu_backward ve ffn_swiglu_backward — FFN Activation Backward"
+ * (https://llm.istanbul/learn/tr/09_backward_ffn), section "Türevler / SiLU'".
+ * The SwiGLU combine is applied while the A operand is staged, so the hidden
+ * [M x K] matrix is never written ("Önemli Optimizasyonlar" §3 of the first
+ * page).
+ *
+ * Layout.  Every array is dense and row-major with no strides:
+ *   X, GATE, UP : [M x K] fp32          W : [K x N] fp32 or binary16
+ *   R, Y        : [M x N] fp32
+ * W is [in x out] as in the page's "Bind Group ABI" (not PyTorch's
+ * [out x in] Linear weight).  Arithmetic: fp32 products and fp32 accumulation
+ * on the matrix cores; binary16 weights are widened exactly to fp32 before use.
+ *
+ * Ownership.  All array pointers are device pointers owned by the caller.  The
+ * library never allocates, frees or keeps device memory.  A call only enqueues
+ * work on `stream` (a hipStream_t; NULL means the null stream) and returns;
+ * inputs must stay valid and unmodified, and Y must not be read, until the
+ * stream has passed the kernel.  Only Y[i][j] for i < M, j < N is written, and
+ * nothing outside the inputs is read.  Results are bitwise reproducible from
+ * run to run for the same inputs, shape and configuration.
+ *
+ * Errors.  Arguments are validated synchronously before anything is enqueued;
+ * on a negative status nothing is launched and Y is untouched.  No exception or
+ * abort crosses this interface.  Calls may be made from several host threads;
+ * the library has no mutable global state.
+ *
+ * Preconditions (the page's host-side rule that K and N be multiples of 4 for
+ * the 16-byte vector loads, "Önemli Optimizasyonlar" §1):
+ *   0 <= M, K, N < 2^31;  K % 4 == 0;  N % 4 == 0;
+ *   fp32 arrays 16-byte aligned; binary16 W 8-byte aligned;
+ *   Y overlaps none of the inputs (R included).
+ * Degenerate shapes: M == 0 or N == 0 enqueues nothing and returns GEMM_OK;
+ * K == 0 gives Y = R (or Y = 0 without a residual).  The pointer of an array
+ * with no elements (e.g. X and W when K == 0) may be NULL.
+ */
+#ifndef GEMM_FWD_H
+#define GEMM_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GEMM_OK 0
+#define GEMM_ERR_NULL (-1)   /* NULL pointer for a non-empty array (R is required by gemm_fwd_swiglu) */
+#define GEMM_ERR_SHAPE (-2)  /* negative or too-large dimension, or K % 4 != 0, or N % 4 != 0 */
+#define GEMM_ERR_ALIGN (-3)  /* fp32 array not 16-byte aligned, or binary16 W not 8-byte aligned */
+#define GEMM_ERR_DTYPE (-4)  /* unknown flag bits or w_dtype */
+#define GEMM_ERR_ALIAS (-5)  /* Y overlaps an input */
+#define GEMM_ERR_LAUNCH (-6) /* the HIP runtime reported an error at launch */
+#define GEMM_ERR_CONFIG (-7) /* an explicit tile configuration index is out of range */
+
+/* gemm_fwd flags. */
+#define GEMM_FLAG_W_F16 0x1u /* W holds IEEE binary16 values; otherwise fp32 */
+
+/* gemm_fwd_swiglu weight types. */
+#define GEMM_W_F32 0
+#define GEMM_W_F16 1
+
+/*
+ * matmul / matmul_residual / matmul_w16 / matmul_residual_w16.
+ *   X [M x K] fp32, W [K x N] (fp32, or binary16 with GEMM_FLAG_W_F16),
+ *   R [M x N] fp32 or NULL (no residual), Y [M x N] fp32 (output).
+ *   Y = X @ W (+ R).
+ * Returns GEMM_OK or a negative status.
+ */
+int gemm_fwd(const float *X, const void *W, const float *R, float *Y,
+             int64_t M, int64_t K, int64_t N, uint32_t flags, void *stream);
+
+/*
+ * matmul_residual_swiglu_a / matmul_residual_swiglu_a_w16.
+ *   GATE, UP [M x K] fp32, W [K x N] (w_dtype GEMM_W_F32 or GEMM_W_F16),
+ *   R [M x N] fp32 (required), Y [M x N] fp32 (output).
+ *   Y = (silu(GATE) * UP) @ W + R, the combine applied as A is staged.
+ * Returns GEMM_OK or a negative status.
+ */
+int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                    int64_t M, int64_t K, int64_t N, int w_dtype, void *stream);
+
+/*
+ * Same operations with an explicit tile configuration (config >= 0, an index
+ * below gemm_num_configs()), or the library's own choice (config < 0).  Every
+ * configuration computes the same function; they differ in tile shape and
+ * speed, and results may differ in the last bits between configurations.
+ * Used by tuning sweeps and by tests that cover every kernel instantiation.
+ */
+int gemm_fwd_cfg(const float *X, const void *W, const float *R, float *Y,
+                 int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream);
+int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                        int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream);
+
+/* Number of tile configurations compiled into the library. */
+int gemm_num_configs(void);
+
+/* Static name of a configuration ("BMxBNxBK_..."), or NULL if out of range. */
+const char *gemm_config_name(int config);
+
+/* The configuration the library picks for a shape (swiglu, w_f16 are 0/1). */
+int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16);
+
+/* Static text for a status code. */
+const char *gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_FWD_H */

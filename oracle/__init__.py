@@ -76,6 +76,8 @@ def configure(lib):
     lib.oracle_a_rows.restype = c_int
     lib.oracle_gemm_rows_f64a.argtypes = [p, p, c_int, p, i64, i64, i64, p, c_int]
     lib.oracle_gemm_rows_f64a.restype = c_int
+    lib.oracle_row_col_sums.argtypes = [p, p, p, c_int, p, i64, i64, i64, p, p, p, p, c_int]
+    lib.oracle_row_col_sums.restype = c_int
     return lib
 
 
@@ -164,6 +166,60 @@ def gemm_f64a(H, W, R=None, threads=0):
     if rc != 0:
         raise ValueError(f"oracle_gemm_rows_f64a rejected its arguments (rc={rc})")
     return y
+
+
+def row_col_sums(A, W, R=None, U=None, threads=0):
+    """Exact-in-fp64 row and column sums of the product and their magnitudes.
+
+    Returns (row_sum [M], row_mag [M], col_sum [N], col_mag [N]) where
+    row_sum[i] = sum_j y_ij, row_mag[i] = sum_j sum_k |a_ik||w_kj|, and the
+    same over i for columns (R's sums are included in row_sum/col_sum).
+    """
+    A = _f32(A, "A")
+    U = _f32(U, "U")
+    R = _f32(R, "R")
+    M, K = A.shape
+    N = W.shape[1]
+    rs, rm = np.empty(M), np.empty(M)
+    cs, cm = np.empty(N), np.empty(N)
+    rc = _load().oracle_row_col_sums(_ptr(A), _ptr(U), _ptr(W), int(W.dtype == np.float16), _ptr(R),
+                                     M, K, N, _ptr(rs), _ptr(rm), _ptr(cs), _ptr(cm), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_row_col_sums rejected its arguments (rc={rc})")
+    return rs, rm, cs, cm
+
+
+def compare_sums(y, R, sums, tol):
+    """Check the row and column sums of a result against row_col_sums().
+
+    Each sum may differ by at most rel * (summed tolerance scale) + abs * count,
+    plus 2^-23 * sum |y| for the rounding of the residual add and of y itself.
+    Returns the worst ratio over all rows and columns and the failure count.
+    """
+    rel, ab = tol
+    rs, rm, cs, cm = sums
+    M, N = rs.shape[0], cs.shape[0]
+    y_rows = np.zeros(M)
+    y_rows_abs = np.zeros(M)
+    y_cols = np.zeros(N)
+    y_cols_abs = np.zeros(N)
+    step = max(1, (1 << 24) // max(N, 1))
+    for i0 in range(0, M, step):
+        blk = np.asarray(y[i0:i0 + step], dtype=np.float64)
+        y_rows[i0:i0 + step] = blk.sum(axis=1)
+        y_rows_abs[i0:i0 + step] = np.abs(blk).sum(axis=1)
+        y_cols += blk.sum(axis=0)
+        y_cols_abs += np.abs(blk).sum(axis=0)
+    r_bound = rel * rm + ab * N + 2.0 ** -23 * y_rows_abs
+    c_bound = rel * cm + ab * M + 2.0 ** -23 * y_cols_abs
+    with np.errstate(invalid="ignore"):
+        r_ratio = np.abs(y_rows - rs) / r_bound
+        c_ratio = np.abs(y_cols - cs) / c_bound
+    r_ratio = np.where(np.isfinite(r_ratio), r_ratio, np.inf)
+    c_ratio = np.where(np.isfinite(c_ratio), c_ratio, np.inf)
+    worst = max(float(r_ratio.max(initial=0.0)), float(c_ratio.max(initial=0.0)))
+    fails = int(np.count_nonzero(r_ratio > 1.0) + np.count_nonzero(c_ratio > 1.0))
+    return {"max_ratio": worst, "fails": fails}
 
 
 def compare(y, y_ref, scale, tol):

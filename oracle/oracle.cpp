@@ -152,6 +152,82 @@ int oracle_gemm_rows(const float *A, const float *U, const void *W, int w_is_f16
     return 0;
 }
 
+// Row and column sums of the product, from linearity of the definition above:
+//   sum_j Y[i,j] = sum_k a_{i,k} * (sum_j w_{k,j})  + sum_j R[i,j]
+//   sum_i Y[i,j] = sum_k (sum_i a_{i,k}) * w_{k,j}  + sum_i R[i,j]
+// with the matching magnitudes (the tolerance scale summed over the same
+// index):
+//   row_mag[i] = sum_k |a_{i,k}| * sum_j |w_{k,j}|
+//   col_mag[j] = sum_k (sum_i |a_{i,k}|) * |w_{k,j}|
+// They cost O(MK + KN) instead of O(MKN), so every row and every column of a
+// full-size result can be checked.  Any output pointer may be NULL.
+int oracle_row_col_sums(const float *A, const float *U, const void *W, int w_is_f16,
+                        const float *R, int64_t M, int64_t K, int64_t N,
+                        double *row_sum, double *row_mag, double *col_sum, double *col_mag,
+                        int nthreads) {
+    if (A == nullptr || W == nullptr || M < 0 || K < 0 || N < 0) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    std::vector<double> wsum(static_cast<size_t>(K)), wabs(static_cast<size_t>(K));
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0, a = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const size_t idx = static_cast<size_t>(k) * N + j;
+            const double w = w_is_f16
+                ? oracle_half_to_double(static_cast<const uint16_t *>(W)[idx])
+                : static_cast<double>(static_cast<const float *>(W)[idx]);
+            s += w;
+            a += std::fabs(w);
+        }
+        wsum[k] = s;
+        wabs[k] = a;
+    }
+    // per-row pass: row sums, and per-thread column sums of a and |a|
+    std::vector<double> asum(static_cast<size_t>(K), 0.0), aabs(static_cast<size_t>(K), 0.0);
+#pragma omp parallel num_threads(nthreads)
+    {
+        std::vector<double> ls(static_cast<size_t>(K), 0.0), la(static_cast<size_t>(K), 0.0);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            double s = 0.0, m = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = a_value(A, U, i * K + k);
+                s += a * wsum[k];
+                m += std::fabs(a) * wabs[k];
+                ls[k] += a;
+                la[k] += std::fabs(a);
+            }
+            double rs = 0.0;
+            for (int64_t j = 0; R != nullptr && j < N; ++j) rs += static_cast<double>(R[i * N + j]);
+            if (row_sum) row_sum[i] = s + rs;
+            if (row_mag) row_mag[i] = m;
+        }
+#pragma omp critical
+        for (int64_t k = 0; k < K; ++k) {
+            asum[k] += ls[k];
+            aabs[k] += la[k];
+        }
+    }
+    if (col_sum == nullptr && col_mag == nullptr) return 0;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t j = 0; j < N; ++j) {
+        double s = 0.0, m = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const size_t idx = static_cast<size_t>(k) * N + j;
+            const double w = w_is_f16
+                ? oracle_half_to_double(static_cast<const uint16_t *>(W)[idx])
+                : static_cast<double>(static_cast<const float *>(W)[idx]);
+            s += asum[k] * w;
+            m += aabs[k] * std::fabs(w);
+        }
+        double rs = 0.0;
+        for (int64_t i = 0; R != nullptr && i < M; ++i) rs += static_cast<double>(R[i * N + j]);
+        if (col_sum) col_sum[j] = s + rs;
+        if (col_mag) col_mag[j] = m;
+    }
+    return 0;
+}
+
 // The A operand as the contraction sees it, materialised: H[i,k] = a_{i,k}
 // for the rows selected (rows == NULL: all).  Used by the pins that check
 // swiglu_a(G, U, W, R) == matmul_residual(silu(G)*U, W, R).

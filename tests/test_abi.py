@@ -1,0 +1,143 @@
+"""The C-ABI boundary, on the CPU: the library loads, exports every function
+that include/gemm_fwd.h declares, and rejects bad arguments synchronously with
+the documented status codes before touching any device (all pointers here are
+fake host addresses; no compute call reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_fwd.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_0-9]+)\s*\(", text)))
+
+
+def _status(name):
+    m = re.search(r"#define\s+" + name + r"\s+\(?(-?\d+)\)?", _header_text())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tiled_dense_gemm_matmul_amd import binding
+    return binding.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert {"gemm_fwd", "gemm_fwd_swiglu", "gemm_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libgemmfwd.so does not export {n}"
+
+
+def test_status_codes_match_header(lib):
+    for name in ["GEMM_OK", "GEMM_ERR_NULL", "GEMM_ERR_SHAPE", "GEMM_ERR_ALIGN", "GEMM_ERR_DTYPE",
+                 "GEMM_ERR_ALIAS", "GEMM_ERR_LAUNCH", "GEMM_ERR_CONFIG"]:
+        code = _status(name)
+        text = lib.gemm_status_string(code).decode()
+        assert text and text != "unknown status", name
+    assert lib.gemm_status_string(12345).decode() == "unknown status"
+
+
+def test_config_table(lib):
+    n = lib.gemm_num_configs()
+    assert n >= 1
+    names = [lib.gemm_config_name(i).decode() for i in range(n)]
+    assert len(set(names)) == n
+    assert lib.gemm_config_name(n) is None and lib.gemm_config_name(-1) is None
+    for shape in [(512, 768, 16384), (512, 3072, 768), (128, 768, 768), (8192, 768, 50304), (1, 4, 4)]:
+        for sw in (0, 1):
+            for w16 in (0, 1):
+                assert 0 <= lib.gemm_select_config(*shape, sw, w16) < n
+
+
+# fake, well-aligned, non-overlapping host addresses
+X, W, R, Y, U = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def fwd(lib, x=X, w=W, r=R, y=Y, M=64, K=64, N=64, flags=0, config=-1):
+    return lib.gemm_fwd_cfg(x, w, r, y, M, K, N, flags, config, None)
+
+
+def sw(lib, g=X, u=U, w=W, r=R, y=Y, M=64, K=64, N=64, wd=0, config=-1):
+    return lib.gemm_fwd_swiglu_cfg(g, u, w, r, y, M, K, N, wd, config, None)
+
+
+def test_null_pointers(lib):
+    E = _status("GEMM_ERR_NULL")
+    assert fwd(lib, x=None) == E
+    assert fwd(lib, w=None) == E
+    assert fwd(lib, y=None) == E
+    assert sw(lib, u=None) == E
+    assert sw(lib, r=None) == E  # the residual is required by the SwiGLU variant
+    assert lib.gemm_fwd(None, W, None, Y, 4, 4, 4, 0, None) == E
+    # arrays with no elements may have NULL storage (empty tensors)
+    OK = _status("GEMM_OK")
+    assert fwd(lib, x=None, y=None, M=0) == OK
+    assert fwd(lib, w=None, y=None, N=0) == OK
+    assert sw(lib, g=None, u=None, w=None, r=None, y=None, M=0, N=0) == OK
+
+
+def test_shapes(lib):
+    E = _status("GEMM_ERR_SHAPE")
+    assert fwd(lib, K=6) == E
+    assert fwd(lib, N=66) == E
+    assert fwd(lib, M=-1) == E
+    assert fwd(lib, K=-4) == E
+    assert fwd(lib, N=1 << 31) == E
+    assert sw(lib, K=3074) == E
+
+
+def test_alignment(lib):
+    E = _status("GEMM_ERR_ALIGN")
+    assert fwd(lib, x=X + 4) == E
+    assert fwd(lib, y=Y + 8) == E
+    assert fwd(lib, r=R + 12) == E
+    assert fwd(lib, w=W + 8) == E                        # fp32 W needs 16 bytes
+    assert fwd(lib, w=W + 8, flags=1, M=0) == _status("GEMM_OK")  # f16 W needs only 8 bytes
+    assert fwd(lib, w=W + 4, flags=1) == E
+    assert sw(lib, u=U + 4) == E
+
+
+def test_dtype_and_config(lib):
+    assert fwd(lib, flags=2) == _status("GEMM_ERR_DTYPE")
+    assert sw(lib, wd=2) == _status("GEMM_ERR_DTYPE")
+    assert sw(lib, wd=-1) == _status("GEMM_ERR_DTYPE")
+    assert fwd(lib, config=lib.gemm_num_configs()) == _status("GEMM_ERR_CONFIG")
+
+
+def test_alias(lib):
+    E = _status("GEMM_ERR_ALIAS")
+    M = K = N = 64
+    assert fwd(lib, r=Y) == E                          # in-place residual is rejected
+    assert fwd(lib, x=Y + 16 * 4) == E                  # partial overlap
+    assert fwd(lib, w=Y - 16 * 4) == E
+    assert sw(lib, u=Y + M * N * 4 - 16) == E
+    # adjacent, not overlapping: passes validation (checked on a no-op shape)
+    assert fwd(lib, x=Y + M * N * 4, M=0) == _status("GEMM_OK")
+
+
+def test_degenerate_shapes_are_noops(lib):
+    OK = _status("GEMM_OK")
+    assert fwd(lib, M=0) == OK
+    assert fwd(lib, N=0) == OK
+    assert sw(lib, M=0) == OK
+    assert fwd(lib, M=0, K=0, N=0) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    from tiled_dense_gemm_matmul_amd import binding
+    x = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        binding.matmul(x, x)

@@ -1,0 +1,177 @@
+"""Edge cases of the HIP path: ragged and tiny shapes, K = 0, out-of-bounds
+guards on both sides of every array, exactness on integer inputs and special
+weights, the sigmoid branch far out, binary16 subnormal weights, run-to-run
+determinism and the error path for an aliased output."""
+import numpy as np
+import pytest
+
+import oracle
+from tiled_dense_gemm_matmul_amd import inputs
+
+from _gpu import check, device, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    from tiled_dense_gemm_matmul_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("M", [1, 63, 65, 129])
+@pytest.mark.parametrize("N", [4, 68, 132])
+@pytest.mark.parametrize("K", [4, 20, 772])
+def test_ragged_shapes(M, N, K):
+    say(f"ragged M={M} K={K} N={N}")
+    c = inputs.random_case(M + 1000 * N + K, M, K, N, residual=True)
+    check(c, run(c).cpu().numpy(), label="matmul_residual")
+    c = inputs.random_case(M + 1000 * N + K + 1, M, K, N, swiglu=True, w16=True, residual=True, gate_scale=3.0)
+    check(c, run(c).cpu().numpy(), label="swiglu_w16")
+
+
+def test_k_zero():
+    import torch
+    b = _lib()
+    R = to_dev(np.arange(12, dtype=np.float32).reshape(3, 4))
+    X = torch.zeros((3, 0), dtype=torch.float32, device=device())
+    W = torch.zeros((0, 4), dtype=torch.float32, device=device())
+    y = b.matmul(X, W, R)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), R.cpu())
+    y = b.matmul(X, W)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), torch.zeros(3, 4))
+
+
+def test_empty_outputs():
+    import torch
+    b = _lib()
+    X = torch.zeros((0, 8), dtype=torch.float32, device=device())
+    W = torch.zeros((8, 4), dtype=torch.float32, device=device())
+    assert b.matmul(X, W).shape == (0, 4)
+    X = torch.zeros((5, 8), dtype=torch.float32, device=device())
+    W = torch.zeros((8, 0), dtype=torch.float32, device=device())
+    assert b.matmul(X, W).shape == (5, 0)
+
+
+def _poisoned(a, tail=4096, head=4096):
+    """Device copy of a with NaN-filled neighbours before and after it."""
+    import torch
+    flat = np.ascontiguousarray(a).reshape(-1)
+    buf = torch.full((head + flat.size + tail,), float("nan"), dtype=torch.float32 if a.dtype == np.float32 else torch.float16,
+                     device=device())
+    buf[head:head + flat.size] = torch.from_numpy(flat).to(device())
+    return buf, buf[head:head + flat.size].view(*a.shape)
+
+
+@pytest.mark.parametrize("cfg", [None, 0, 1, 2, 3])
+def test_no_out_of_bounds_reads_or_writes(cfg):
+    import torch
+    b = _lib()
+    if cfg is not None and cfg >= b.num_configs():
+        pytest.skip("no such config")
+    M, K, N = 70, 84, 76
+    say(f"guard bands M={M} K={K} N={N} config={cfg}")
+    for swiglu, w16 in [(False, False), (True, True), (False, True)]:
+        c = inputs.random_case(77, M, K, N, swiglu=swiglu, w16=w16, residual=True, gate_scale=2.0)
+        W = _poisoned(c["W"])[1]
+        R = _poisoned(c["R"])[1]
+        ybuf = torch.full((M * N + 8192,), -777.0, dtype=torch.float32, device=device())
+        y = ybuf[4096:4096 + M * N].view(M, N)
+        if swiglu:
+            b.matmul_residual_swiglu_a(_poisoned(c["G"])[1], _poisoned(c["U"])[1], W, R, out=y, config=cfg)
+        else:
+            b.matmul(_poisoned(c["X"])[1], W, R, out=y, config=cfg)
+        torch.cuda.synchronize()
+        host = ybuf.cpu().numpy()
+        assert np.all(host[:4096] == -777.0) and np.all(host[4096 + M * N:] == -777.0), "write outside Y"
+        yy = host[4096:4096 + M * N].reshape(M, N)
+        assert np.all(np.isfinite(yy)), "NaN from outside an input leaked into Y"
+        check(c, yy, label=f"swiglu={swiglu} w16={w16}")
+
+
+@pytest.mark.parametrize("cfg", [None, 0, 1, 2, 3])
+def test_integer_inputs_bit_exact(cfg):
+    b = _lib()
+    if cfg is not None and cfg >= b.num_configs():
+        pytest.skip("no such config")
+    for (M, K, N) in [(96, 3072, 64), (257, 768, 260)]:
+        for w16 in (False, True):
+            c = inputs.random_case(M + K, M, K, N, w16=w16, residual=True, integer=True)
+            say(f"integer M={M} K={K} N={N} w16={w16} config={cfg}")
+            y = run(c, config=cfg).cpu().numpy()
+            y_ref = oracle.gemm(c["X"], c["W"], R=c["R"])
+            assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_zero_and_identity_weights_bitwise():
+    M, K = 130, 196
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((M, K), dtype=np.float32)
+    R = rng.standard_normal((M, K), dtype=np.float32)
+    zero = {"X": X, "W": np.zeros((K, K), np.float32), "R": R}
+    assert np.array_equal(run(zero).cpu().numpy(), R)
+    eye = {"X": X, "W": np.eye(K, dtype=np.float32)}
+    assert np.array_equal(run(eye).cpu().numpy(), X)
+    eye16 = {"X": X, "W": np.eye(K, dtype=np.float16)}
+    assert np.array_equal(run(eye16).cpu().numpy(), X)
+    G = rng.standard_normal((M, K), dtype=np.float32)
+    sw0 = {"G": G, "U": X, "W": np.zeros((K, K), np.float32), "R": R}
+    assert np.array_equal(run(sw0).cpu().numpy(), R)
+
+
+def test_silu_probe_far_out():
+    """Identity W makes Y = silu(G) * U + R: the sigmoid's two branches at
+    +-80, +-100, +-1000, zero and tiny gates, against the oracle."""
+    K = 64
+    vals = np.array([80, -80, 100, -100, 1000, -1000, 0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0, 89.0, -89.0,
+                     20, -20, 5, -5, 1, -1, 0.5, -0.5, 1e-3, -1e-3], dtype=np.float32)
+    M = 8
+    G = np.resize(vals, (M, K)).astype(np.float32)
+    rng = np.random.default_rng(6)
+    U = rng.standard_normal((M, K), dtype=np.float32)
+    R = rng.standard_normal((M, K), dtype=np.float32)
+    c = {"G": G, "U": U, "W": np.eye(K, dtype=np.float32), "R": R}
+    y = run(c).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    h = oracle.a_operand(G, U)
+    # a handful of fp32 roundings: the exponential, the reciprocal, two products, the add
+    err = np.abs(y.astype(np.float64) - (h + R.astype(np.float64)))
+    assert np.all(err <= 8 * 2.0 ** -24 * (np.abs(h) + np.abs(R)) + 1e-37), float(err.max())
+    check(c, y, label="silu probe")
+
+
+def test_f16_subnormal_weights_are_not_flushed():
+    M, K, N = 64, 64, 64
+    rng = np.random.default_rng(8)
+    X = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    bits = np.zeros((K, N), np.uint16)
+    for j in range(N):
+        bits[(j * 7) % K, j] = 1 + j * 16      # subnormal binary16 (exponent field 0)
+        bits[(j * 3 + 1) % K, j] = 0x8000 | (3 + j)
+    W = bits.view(np.float16)
+    assert np.all(np.abs(W.astype(np.float32)) < 2.0 ** -14)
+    c = {"X": X, "W": W}
+    y = run(c).cpu().numpy()
+    assert np.array_equal(y.astype(np.float64), oracle.gemm(X, W))
+    assert np.count_nonzero(y) > M * N // 2
+
+
+def test_deterministic():
+    c = inputs.cfg3()
+    a = run(c).cpu().numpy()
+    b = run(c).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_aliased_output_is_rejected():
+    b = _lib()
+    c = inputs.random_case(3, 64, 64, 64, residual=True)
+    X, W, R = to_dev(c["X"]), to_dev(c["W"]), to_dev(c["R"])
+    keep = R.clone()
+    with pytest.raises(b.GemmError) as e:
+        b.matmul(X, W, R, out=R)
+    assert e.value.status == -5
+    import torch
+    torch.cuda.synchronize()
+    assert torch.equal(R, keep)

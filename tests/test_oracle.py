@@ -354,6 +354,9 @@ MUTATIONS = [
      [check_binary16_golden, check_bruteforce_rational]),
     ("scale_signed", "const double aik = std::fabs(a[k]);", "const double aik = a[k];",
      [check_bruteforce_integers]),
+    ("rowsum_dropped_residual", "if (row_sum) row_sum[i] = s + rs;", "if (row_sum) row_sum[i] = s;",
+     [lambda o: check_row_col_sums(o)]),
+    ("colsum_wrong_weight", "s += asum[k] * w;", "s += aabs[k] * w;", [lambda o: check_row_col_sums(o)]),
 ]
 
 
@@ -395,5 +398,44 @@ def test_planted_mistakes_are_caught(oracle_mod, tmp_path, name, old, new, pins)
         try:
             pin(mutant)
         except AssertionError:
-            caught.append(pin.__name__)
+            caught.append(getattr(pin, "__name__", "pin"))
     assert caught, f"no pin caught planted mistake {name}"
+
+
+def check_row_col_sums(orc, seed=4):
+    for (M, K, N, sw, w16, res) in [(7, 12, 9, False, False, True), (5, 20, 8, True, True, True),
+                                      (6, 8, 4, False, True, False)]:
+        case = inputs.random_case(seed, M, K, N, swiglu=sw, w16=w16, residual=res)
+        A = case["G"] if sw else case["X"]
+        U = case.get("U")
+        R = case.get("R")
+        y, b = orc.gemm(A, case["W"], R=R, U=U, want_scale=True)
+        rs, rm, cs, cm = orc.row_col_sums(A, case["W"], R=R, U=U)
+        tot = np.abs(y).sum() + b.sum() + 1.0
+        assert np.allclose(rs, y.sum(axis=1), rtol=0, atol=1e-13 * tot)
+        assert np.allclose(cs, y.sum(axis=0), rtol=0, atol=1e-13 * tot)
+        assert np.allclose(rm, b.sum(axis=1), rtol=1e-13)
+        assert np.allclose(cm, b.sum(axis=0), rtol=1e-13)
+        # integers: exact
+    case = inputs.random_case(seed, 6, 16, 10, integer=True, residual=True)
+    X, W, R = case["X"], case["W"], case["R"]
+    rs, rm, cs, cm = orc.row_col_sums(X, W, R=R)
+    Xi, Wi, Ri = X.astype(np.int64), W.astype(np.int64), R.astype(np.int64)
+    Yi = Xi @ Wi + Ri
+    assert np.array_equal(rs, Yi.sum(axis=1).astype(np.float64))
+    assert np.array_equal(cs, Yi.sum(axis=0).astype(np.float64))
+    assert np.array_equal(rm, (np.abs(Xi) @ np.abs(Wi)).sum(axis=1).astype(np.float64))
+
+
+def test_row_col_sums(oracle_mod):
+    check_row_col_sums(oracle_mod)
+
+
+def test_compare_sums_detects_a_wrong_row(oracle_mod):
+    case = inputs.random_case(9, 40, 64, 24, residual=True)
+    y = oracle_mod.gemm(case["X"], case["W"], R=case["R"]).astype(np.float32)
+    sums = oracle_mod.row_col_sums(case["X"], case["W"], R=case["R"])
+    assert oracle_mod.compare_sums(y, case["R"], sums, oracle_mod.TOL_W32)["fails"] == 0
+    y_bad = y.copy()
+    y_bad[13, 5] += 0.01
+    assert oracle_mod.compare_sums(y_bad, case["R"], sums, oracle_mod.TOL_W32)["fails"] >= 2

@@ -1,0 +1,96 @@
+"""GPU parity of the five workloads against the fp64 oracle, element by
+element, in the launch configuration the library selects (the one bench.py
+times).  Tolerances: |y - y_ref| <= 2e-5 * sum_k|a_ik||w_kj| + 1e-6 for fp32
+weights and 1e-3 * sum_k|a_ik||w_kj| + 1e-5 for binary16 weights.
+
+The two largest cases (M = 8192 / 8191) are checked element-wise on a sample
+of rows that includes the whole last (partial) tile, and in every row and
+column through the exact row/column sums of the product."""
+import numpy as np
+import pytest
+
+from tiled_dense_gemm_matmul_amd import inputs
+
+from _gpu import check, check_sums, run, say, to_dev, device
+
+pytestmark = pytest.mark.gpu
+
+
+def _host(y):
+    return y.cpu().numpy()
+
+
+def test_cfg1_matmul():
+    c = inputs.cfg1()
+    say("cfg1 matmul 128x768x768 seed 0")
+    check(c, _host(run(c)), label="cfg1")
+
+
+def test_cfg2_matmul_residual_and_matmul():
+    c = inputs.cfg2()
+    say("cfg2 matmul_residual 512x768x768 seed 1")
+    check(c, _host(run(c)), label="cfg2 +R")
+    c0 = {"X": c["X"], "W": c["W"]}
+    check(c0, _host(run(c0)), label="cfg2 matmul")
+
+
+def test_cfg3_swiglu_down():
+    c = inputs.cfg3()
+    say("cfg3 matmul_residual_swiglu_a 512x3072x768 seed 2 (+-80 gates)")
+    check(c, _host(run(c)), label="cfg3")
+
+
+def test_cfg4_lm_head_and_gate_up_w16():
+    c = inputs.cfg4()
+    lm = {"X": c["X"], "W": c["W_lm"]}
+    say("cfg4 matmul_w16 lm_head 512x768x16384 seed 3")
+    check(lm, _host(run(lm)), label="cfg4 lm_head")
+    gu = {"X": c["X"], "W": c["W_gu"]}
+    say("cfg4b matmul_w16 gate/up 512x768x3072")
+    check(gu, _host(run(gu)), label="cfg4b gate/up")
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    return inputs.cfg5()
+
+
+def _sample_rows(M, seed, count=96):
+    rng = np.random.default_rng(seed)
+    tail_start = (M - 1) // 64 * 64 - 64        # the last two 64-row tiles, whole
+    rows = np.concatenate([rng.choice(tail_start, size=count, replace=False), np.arange(tail_start, M)])
+    return np.unique(rows)
+
+
+def _guarded_run(case, M, N):
+    """Run with Y inside a larger buffer; the 4096 floats after it must stay untouched."""
+    import torch
+    guard = 4096
+    buf = torch.full((M * N + guard,), float("nan"), dtype=torch.float32, device=device())
+    buf[M * N:] = 12345.0
+    y = buf[: M * N].view(M, N)
+    run(case, out=y)
+    tail = buf[M * N:].cpu().numpy()
+    assert np.all(tail == 12345.0), "write past the end of Y"
+    return y
+
+
+@pytest.mark.parametrize("M", [8192, 8191])
+def test_cfg5a_swiglu_down_w16(cfg5, M):
+    c = {"G": np.ascontiguousarray(cfg5["G"][:M]), "U": np.ascontiguousarray(cfg5["U"][:M]),
+         "W": cfg5["W_down"], "R": np.ascontiguousarray(cfg5["R"][:M])}
+    say(f"cfg5a matmul_residual_swiglu_a_w16 {M}x3072x768 seed 4")
+    y = _host(_guarded_run(c, M, 768))
+    rows = _sample_rows(M, 50 + M)
+    check(c, y[rows], rows=rows, label=f"cfg5a M={M} sampled rows")
+    check_sums(c, y, label=f"cfg5a M={M}")
+
+
+@pytest.mark.parametrize("M", [8192, 8191])
+def test_cfg5b_lm_head_w16(cfg5, M):
+    c = {"X": np.ascontiguousarray(cfg5["X"][:M]), "W": cfg5["W_lm"]}
+    say(f"cfg5b matmul_w16 lm_head {M}x768x50304 seed 4")
+    y = _host(_guarded_run(c, M, 50304))
+    rows = _sample_rows(M, 70 + M, count=32)
+    check(c, y[rows], rows=rows, label=f"cfg5b M={M} sampled rows")
+    check_sums(c, y, label=f"cfg5b M={M}")

@@ -13,6 +13,7 @@ The binding (and with it torch and the HIP library) is loaded on first use, so
 _BINDING_NAMES = {
     "matmul", "matmul_residual", "matmul_residual_swiglu_a", "gemm_fwd", "gemm_fwd_swiglu",
     "status_string", "library_path", "load_library", "GemmError", "kernel_config",
+    "num_configs", "config_name",
     "GEMM_FLAG_W_F16", "GEMM_W_F32", "GEMM_W_F16",
 }
 

@@ -1,0 +1,183 @@
+"""Python binding over libgemmfwd.so (the C ABI declared in include/gemm_fwd.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, pointers and
+the current HIP stream are passed through, and every step of the computation
+runs in the library's HIP kernels.  torch provides device memory and streams.
+The library must be built (``__graft_entry__.build()``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+GEMM_FLAG_W_F16 = 0x1
+GEMM_W_F32 = 0
+GEMM_W_F16 = 1
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmfwd.so")
+_lib = None
+
+EXPORTED = (
+    "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_cfg", "gemm_fwd_swiglu_cfg",
+    "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgemmfwd.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i64, u32, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int
+    lib.gemm_fwd.argtypes = [p, p, p, p, i64, i64, i64, u32, p]
+    lib.gemm_fwd.restype = c_int
+    lib.gemm_fwd_swiglu.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, p]
+    lib.gemm_fwd_swiglu.restype = c_int
+    lib.gemm_fwd_cfg.argtypes = [p, p, p, p, i64, i64, i64, u32, c_int, p]
+    lib.gemm_fwd_cfg.restype = c_int
+    lib.gemm_fwd_swiglu_cfg.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, c_int, p]
+    lib.gemm_fwd_swiglu_cfg.restype = c_int
+    lib.gemm_num_configs.argtypes = []
+    lib.gemm_num_configs.restype = c_int
+    lib.gemm_config_name.argtypes = [c_int]
+    lib.gemm_config_name.restype = ctypes.c_char_p
+    lib.gemm_select_config.argtypes = [i64, i64, i64, c_int, c_int]
+    lib.gemm_select_config.restype = c_int
+    lib.gemm_status_string.argtypes = [c_int]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gemm_status_string(int(status)).decode()
+
+
+def num_configs() -> int:
+    return load_library().gemm_num_configs()
+
+
+def config_name(config: int):
+    name = load_library().gemm_config_name(int(config))
+    return None if name is None else name.decode()
+
+
+def kernel_config(M, K, N, swiglu=False, w16=False) -> str:
+    """Name of the tile configuration the library picks for a shape."""
+    return config_name(load_library().gemm_select_config(M, K, N, int(swiglu), int(w16)))
+
+
+# --- raw pointer-level calls (same names and argument order as the C ABI) ---
+
+def gemm_fwd(X, W, R, Y, M, K, N, flags, stream, config=-1) -> int:
+    lib = load_library()
+    if config is None or config < 0:
+        return lib.gemm_fwd(X, W, R, Y, M, K, N, flags, stream)
+    return lib.gemm_fwd_cfg(X, W, R, Y, M, K, N, flags, config, stream)
+
+
+def gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream, config=-1) -> int:
+    lib = load_library()
+    if config is None or config < 0:
+        return lib.gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream)
+    return lib.gemm_fwd_swiglu_cfg(G, U, W, R, Y, M, K, N, w_dtype, config, stream)
+
+
+# --- tensor-level API ---
+
+def _check_act(t, name, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_w(W, K, device):
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise TypeError("W must be a 2-D torch.Tensor [K, N]")
+    if W.device != device:
+        raise ValueError(f"W must live on {device}, got {W.device}")
+    if W.dtype not in (torch.float32, torch.float16):
+        raise TypeError(f"W must be float32 or float16, got {W.dtype}")
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous (row-major [K, N])")
+    if W.shape[0] != K:
+        raise ValueError(f"W has {W.shape[0]} rows, expected K={K}")
+    return W.shape[1]
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def matmul(X, W, R=None, out=None, config=None):
+    """Y = X @ W (+ R).  X [M, K] f32, W [K, N] f32 or f16, R [M, N] f32 or None."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise TypeError("X must be a 2-D torch.Tensor [M, K]")
+    M, K = X.shape
+    device = X.device
+    _check_act(X, "X", (M, K), device)
+    N = _check_w(W, K, device)
+    if R is not None:
+        _check_act(R, "R", (M, N), device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=device)
+    else:
+        _check_act(out, "out", (M, N), device)
+    flags = GEMM_FLAG_W_F16 if W.dtype == torch.float16 else 0
+    st = gemm_fwd(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), out.data_ptr(),
+                  M, K, N, flags, _stream(device), -1 if config is None else config)
+    if st != 0:
+        raise GemmError(st, "gemm_fwd")
+    return out
+
+
+def matmul_residual(X, W, R, out=None, config=None):
+    """Y = X @ W + R."""
+    if R is None:
+        raise ValueError("matmul_residual needs R")
+    return matmul(X, W, R, out=out, config=config)
+
+
+def matmul_residual_swiglu_a(G, U, W, R, out=None, config=None):
+    """Y = (silu(G) * U) @ W + R, the SwiGLU combine fused into the A load."""
+    if not isinstance(G, torch.Tensor) or G.dim() != 2:
+        raise TypeError("G must be a 2-D torch.Tensor [M, K]")
+    M, K = G.shape
+    device = G.device
+    _check_act(G, "G", (M, K), device)
+    _check_act(U, "U", (M, K), device)
+    N = _check_w(W, K, device)
+    _check_act(R, "R", (M, N), device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=device)
+    else:
+        _check_act(out, "out", (M, N), device)
+    w_dtype = GEMM_W_F16 if W.dtype == torch.float16 else GEMM_W_F32
+    st = gemm_fwd_swiglu(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(),
+                         M, K, N, w_dtype, _stream(device), -1 if config is None else config)
+    if st != 0:
+        raise GemmError(st, "gemm_fwd_swiglu")
+    return out

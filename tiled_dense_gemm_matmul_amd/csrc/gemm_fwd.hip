@@ -1,0 +1,471 @@
+// Forward linear-layer GEMM family for MI355X (gfx950): HIP kernels + C ABI.
+//
+// Operations ("matmul ve matmul_residual — Tiled Matrix Multiply (Forward)",
+// https://llm.istanbul/learn/tr/03_linear_forward, section "Ne Yapar?"):
+//   Y = A @ W (+ R),  A = X  or  A = silu(GATE) * UP,  W fp32 or binary16.
+//
+// Design (gfx950, wave64, fp32 matrix cores):
+//  * One workgroup owns one BM x BN output tile over the whole K range (the
+//    page's "Tile Hiyerarşisi"), so there are no atomics and no workspace and
+//    every run gives the same bits.
+//  * The contraction runs on v_mfma_f32_16x16x4_f32.  Within a 16-wide slice
+//    of K each lane feeds four consecutive k values (one float4) to four
+//    MFMAs; the pairing of k with lanes is the same for A and B, so the sum
+//    covers every k exactly once.
+//  * A and B tiles are staged through LDS, both stored k-contiguous ("K-major"),
+//    BK floats per row, float4 slots XOR-swizzled by the row index so that the
+//    16-byte LDS writes and the MFMA fragment reads are free of bank conflicts
+//    without padding (the page pads its A tile to 17 for the same purpose).
+//  * Global loads are 16-byte (8-byte for four binary16 weights) and
+//    coalesced along the contiguous dimension.  The W tile is transposed in
+//    registers (4 x 4 blocks) on its way into LDS; binary16 weights are widened
+//    to fp32 there, and the SwiGLU combine silu(g) * u is applied to A there,
+//    so the LDS tiles always hold the exact fp32 operands.
+//  * Two LDS stages, register prefetch: the loads for stage s+1 are issued
+//    before the MFMAs of stage s and written to the other stage after them;
+//    one barrier per stage (the page's "Çift Arabelleğe Alma").
+//  * Small output grids split K across the four waves of a workgroup; their
+//    partial tiles are added through LDS in a fixed order.
+//  * Workgroups are handed to the 8 XCDs round-robin; the tile order is
+//    renumbered so that each XCD works on a contiguous, M-grouped range of
+//    tiles and its private L2 sees reuse of both operands.
+//  * Edges: rows >= M, columns >= N and k >= K are staged as zeros and never
+//    read; stores are masked to i < M, j < N.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gemm_fwd.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+struct Params {
+    const float *A;  // X, or GATE
+    const float *U;  // UP (SwiGLU only)
+    const void *W;
+    const float *R;
+    float *Y;
+    int M, K, N;
+    int tiles_m, tiles_n;
+    int group_m;     // M-tiles per group in the tile order
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Slot permutation of a K-major LDS row: float4 slot s of row r lives at
+// s ^ swz(r).  For 8 consecutive rows, and for 8 rows spaced 4 apart, the
+// values are all distinct, which keeps both the fragment reads (consecutive
+// rows) and the transposed W writes (rows 4 apart) on distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
+
+// silu(g) * u with the sign-branched sigmoid ("ffn_gelu_backward ve
+// ffn_swiglu_backward — FFN Activation Backward", "Türevler / SiLU'"):
+// e = exp(-|g|) is exp(-g) for g >= 0 and exp(g) for g < 0, so the
+// exponential never sees a positive argument and nothing is clamped;
+// sigmoid = 1/(1+e) for g >= 0 and e/(1+e) for g < 0.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __expf(-__builtin_fabsf(g));
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    const float s = g >= 0.0f ? r : e * r;
+    return (g * s) * u;
+}
+
+// Block index -> (tile_m, tile_n).  Consecutive workgroup ids go to XCDs
+// 0..7 in turn; renumber so that XCD x owns the contiguous range
+// [x*q + min(x, r), ...) of the tile order, then walk that order in groups
+// of group_m M-tiles (M fastest inside a group) for L2 reuse.
+__device__ __forceinline__ void tile_coords(const Params &p, int &tm, int &tn) {
+    const int nb = gridDim.x;
+    const int b = blockIdx.x;
+    const int q = nb >> 3, r = nb & 7, x = b & 7;
+    const int t = x * q + (x < r ? x : r) + (b >> 3);
+    const int per_group = p.group_m * p.tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * p.group_m;
+    const int rows = min(p.tiles_m - first_m, p.group_m);
+    const int in_g = t - g * per_group;
+    tm = first_m + in_g % rows;
+    tn = in_g / rows;
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int MINB_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WM = WM_, WN = WN_, WK = WK_;  // waves along M, N, K
+    static constexpr int NT = 64 * WM * WN * WK;
+    static constexpr int MINB = MINB_;                  // workgroups per CU hint
+};
+
+template <bool W16> struct BRegs;
+template <> struct BRegs<false> { f32x4 v[4]; };
+template <> struct BRegs<true> { f16x4 v[4]; };
+
+template <class C, bool SWIGLU, bool W16, bool RESID>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK;
+    constexpr int WM = C::WM, WN = C::WN, WK = C::WK, NT = C::NT;
+    constexpr int SL = BK / 4;              // float4 slots per LDS row
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    constexpr int CH = BK / 16;             // 16-wide k slices per stage
+    constexpr int A_F4 = BM * SL;           // float4s of A per stage
+    constexpr int A_IT = (A_F4 + NT - 1) / NT;
+    constexpr int NQ = BN / 4;
+    constexpr int B_MB = (BK / 4) * NQ;     // 4x4 blocks of W per stage
+    constexpr int B_IT = (B_MB + NT - 1) / NT;
+    constexpr int STAGE = (BM + BN) * BK;   // floats per LDS stage
+    constexpr int RED = (WK - 1) * BM * BN; // floats for the K-split reduction
+    constexpr int LDS_FLOATS = (2 * STAGE > RED) ? 2 * STAGE : RED;
+    static_assert(BK % 32 == 0, "swizzle needs at least 8 slots per row");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be MFMA tiles");
+    static_assert(CH % WK == 0, "K slices must split evenly over waves");
+
+    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wk = wave % WK;
+    const int wmn = wave / WK;
+    const int wm = wmn / WN, wn = wmn % WN;
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, K = p.K, N = p.N;
+
+    const float *Atile = p.A + (size_t)m0 * K;
+    const float *Utile = SWIGLU ? p.U + (size_t)m0 * K : nullptr;
+
+    f32x4 ra[A_IT];
+    f32x4 ru[SWIGLU ? A_IT : 1];
+    BRegs<W16> rb[B_IT];
+
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_IT; ++i) {
+            const int f = tid + i * NT;
+            const int row = f / SL, slot = f % SL;
+            const int gk = k0 + slot * 4;
+            const bool ok = (A_IT * NT == A_F4 || f < A_F4) && (m0 + row < M) && (gk < K);
+            const int off = row * K + gk;
+            ra[i] = ok ? *reinterpret_cast<const f32x4 *>(Atile + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SWIGLU)
+                ru[i] = ok ? *reinterpret_cast<const f32x4 *>(Utile + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < B_IT; ++i) {
+            const int mb = tid + i * NT;
+            const int kq = mb / NQ, nq = mb % NQ;
+            const int gk = k0 + kq * 4, gn = n0 + nq * 4;
+            const bool ok = (B_IT * NT == B_MB || mb < B_MB) && (gk < K) && (gn < N);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const size_t off = (size_t)(gk + j) * N + gn;
+                if constexpr (W16) {
+                    rb[i].v[j] = ok ? *reinterpret_cast<const f16x4 *>(static_cast<const _Float16 *>(p.W) + off)
+                                    : f16x4{0, 0, 0, 0};
+                } else {
+                    rb[i].v[j] = ok ? *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.W) + off)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    };
+
+    auto store_stage = [&](int buf) {
+        float *As = lds + buf * STAGE;
+        float *Bs = As + BM * BK;
+#pragma unroll
+        for (int i = 0; i < A_IT; ++i) {
+            const int f = tid + i * NT;
+            if (A_IT * NT != A_F4 && f >= A_F4) continue;
+            const int row = f / SL, slot = f % SL;
+            f32x4 v = ra[i];
+            if constexpr (SWIGLU) {
+                v.x = silu_mul(v.x, ru[i].x);
+                v.y = silu_mul(v.y, ru[i].y);
+                v.z = silu_mul(v.z, ru[i].z);
+                v.w = silu_mul(v.w, ru[i].w);
+            }
+            *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < B_IT; ++i) {
+            const int mb = tid + i * NT;
+            if (B_IT * NT != B_MB && mb >= B_MB) continue;
+            const int kq = mb / NQ, nq = mb % NQ;
+            float w[4][4];  // w[j][c] = W[4kq + j][4nq + c]
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[j][c] = static_cast<float>(rb[i].v[j][c]);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int n = nq * 4 + c;
+                const f32x4 t = {w[0][c], w[1][c], w[2][c], w[3][c]};
+                *reinterpret_cast<f32x4 *>(Bs + (n * SL + (kq ^ swz(n))) * 4) = t;
+            }
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15, q4 = lane >> 4;
+    auto compute_stage = [&](int buf) {
+        const float *As = lds + buf * STAGE;
+        const float *Bs = As + BM * BK;
+#pragma unroll
+        for (int c = wk; c < CH; c += WK) {
+            const int slot = c * 4 + q4;
+            f32x4 af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 16 + r16;
+                af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = wn * WTN + j * 16 + r16;
+                bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (col * SL + (slot ^ swz(col))) * 4);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][t], bf[j][t], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int nstages = (K + BK - 1) / BK;
+    if (nstages > 0) {
+        load_stage(0);
+        store_stage(0);
+        __syncthreads();
+        for (int s = 0; s < nstages; ++s) {
+            const bool more = s + 1 < nstages;
+            if (more) load_stage((s + 1) * BK);
+            compute_stage(s & 1);
+            if (more) store_stage((s + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    if constexpr (WK > 1) {
+        // Waves 1..WK-1 of each (wm, wn) park their partial tiles in LDS (the
+        // last barrier of the K loop has retired every read of the stages);
+        // wave 0 adds them in the fixed order 1, 2, ..., WK-1.
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+        constexpr int PART = TM * TN * 64;  // float4s per wave partial
+        if (wk > 0) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    red[((wk - 1) * WM * WN + wmn) * PART + (i * TN + j) * 64 + lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (wk != 0) return;
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] += red[((w - 1) * WM * WN + wmn) * PART + (i * TN + j) * 64 + lane];
+    }
+
+    // Epilogue: lane holds rows 4*q4 .. 4*q4+3 of column r16 of each 16x16
+    // MFMA tile.  Y = acc (+ R), masked to the matrix.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + r16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * WTM + i * 16 + q4 * 4 + r;
+                if (row < M && col < N) {
+                    const size_t off = (size_t)row * N + col;
+                    float v = acc[i][j][r];
+                    if constexpr (RESID) v += p.R[off];
+                    p.Y[off] = v;
+                }
+            }
+        }
+    }
+}
+
+// Y = R (or 0) when K == 0: the contraction is empty.
+__global__ void fill_k0_kernel(const float *R, float *Y, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) Y[i] = R ? R[i] : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// configuration table
+// ---------------------------------------------------------------------------
+
+typedef void (*KernelFn)(Params);
+
+struct ConfigEntry {
+    const char *name;
+    int bm, bn, nt;
+    KernelFn fn[2][2][2];  // [swiglu][w16][resid]
+};
+
+template <class C>
+constexpr ConfigEntry make_entry(const char *name) {
+    return ConfigEntry{name, C::BM, C::BN, C::NT,
+                       {{{gemm_fwd_kernel<C, false, false, false>, gemm_fwd_kernel<C, false, false, true>},
+                         {gemm_fwd_kernel<C, false, true, false>, gemm_fwd_kernel<C, false, true, true>}},
+                        {{gemm_fwd_kernel<C, true, false, false>, gemm_fwd_kernel<C, true, false, true>},
+                         {gemm_fwd_kernel<C, true, true, false>, gemm_fwd_kernel<C, true, true, true>}}}};
+}
+
+const ConfigEntry kConfigs[] = {
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 2>>("128x128x32_w2x2"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 2>>("64x64x64_w2x2"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 1>>("32x48x128_k4"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 1>>("64x48x64_w2x1_k2"),
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
+    (void)K; (void)swiglu; (void)w16;
+    const int64_t big = ceil_div(M, 128) * ceil_div(N, 128);
+    if (big >= 256) return 0;
+    const int64_t mid = ceil_div(M, 64) * ceil_div(N, 64);
+    if (mid >= 192) return 1;
+    return 2;
+}
+
+// ---------------------------------------------------------------------------
+// validation + launch
+// ---------------------------------------------------------------------------
+
+bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
+    if (a == nullptr || b == nullptr || abytes == 0 || bbytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, const float *R, float *Y,
+        int64_t M, int64_t K, int64_t N, int config, void *stream) {
+    const int64_t lim = (int64_t)1 << 31;
+    if (M < 0 || K < 0 || N < 0 || M >= lim || K >= lim || N >= lim) return GEMM_ERR_SHAPE;
+    // A pointer may be NULL only when its array holds no element (an empty
+    // tensor has no storage); the residual of the SwiGLU variant is required.
+    const bool mk = M > 0 && K > 0, kn = K > 0 && N > 0, mn = M > 0 && N > 0;
+    if ((mk && A == nullptr) || (kn && W == nullptr) || (mn && Y == nullptr) ||
+        (swiglu && ((mk && U == nullptr) || (mn && R == nullptr))))
+        return GEMM_ERR_NULL;
+    if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
+    // in-tile offsets (row * K + k, k * N + n within a stage) are 32-bit
+    if (K > 0 && 256 * K >= lim) return GEMM_ERR_SHAPE;
+    if (N > 0 && 256 * N >= lim) return GEMM_ERR_SHAPE;
+    if (config >= kNumConfigs) return GEMM_ERR_CONFIG;
+    if ((A && !aligned(A, 16)) || (Y && !aligned(Y, 16)) || (U && !aligned(U, 16)) || (R && !aligned(R, 16)) ||
+        (W && !aligned(W, w16 ? 8 : 16)))
+        return GEMM_ERR_ALIGN;
+    const size_t ybytes = (size_t)M * N * 4, abytes = (size_t)M * K * 4;
+    const size_t wbytes = (size_t)K * N * (w16 ? 2 : 4);
+    if (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, U, abytes) ||
+        overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, R, ybytes))
+        return GEMM_ERR_ALIAS;
+    if (M == 0 || N == 0) return GEMM_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        const int64_t count = M * N;
+        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, R, Y, count);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+
+    const int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
+    const ConfigEntry &e = kConfigs[cfg];
+    Params p;
+    p.A = A; p.U = U; p.W = W; p.R = R; p.Y = Y;
+    p.M = (int)M; p.K = (int)K; p.N = (int)N;
+    p.tiles_m = (int)ceil_div(M, e.bm);
+    p.tiles_n = (int)ceil_div(N, e.bn);
+    p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
+    const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n;
+    if (blocks >= lim) return GEMM_ERR_SHAPE;
+    KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, p);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_fwd_cfg(const float *X, const void *W, const float *R, float *Y,
+                 int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream) {
+    if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
+    return run(false, X, nullptr, W, (flags & GEMM_FLAG_W_F16) != 0, R, Y, M, K, N, config, stream);
+}
+
+int gemm_fwd(const float *X, const void *W, const float *R, float *Y,
+             int64_t M, int64_t K, int64_t N, uint32_t flags, void *stream) {
+    return gemm_fwd_cfg(X, W, R, Y, M, K, N, flags, -1, stream);
+}
+
+int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                        int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream) {
+    if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
+    return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, config, stream);
+}
+
+int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                    int64_t M, int64_t K, int64_t N, int w_dtype, void *stream) {
+    return gemm_fwd_swiglu_cfg(GATE, UP, W, R, Y, M, K, N, w_dtype, -1, stream);
+}
+
+int gemm_num_configs(void) { return kNumConfigs; }
+
+const char *gemm_config_name(int config) {
+    return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : nullptr;
+}
+
+int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16) {
+    return select_config(M, K, N, swiglu, w_f16);
+}
+
+const char *gemm_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "ok";
+        case GEMM_ERR_NULL: return "a required pointer is NULL";
+        case GEMM_ERR_SHAPE: return "bad shape (negative or too large, or K or N not a multiple of 4)";
+        case GEMM_ERR_ALIGN: return "misaligned array (fp32 needs 16 bytes, binary16 W needs 8)";
+        case GEMM_ERR_DTYPE: return "unknown flags or weight type";
+        case GEMM_ERR_ALIAS: return "output overlaps an input";
+        case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        case GEMM_ERR_CONFIG: return "tile configuration index out of range";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"
