@@ -12,15 +12,18 @@
 //    of K each lane feeds four consecutive k values (one float4) to four
 //    MFMAs; the pairing of k with lanes is the same for A and B, so the sum
 //    covers every k exactly once.
-//  * A and B tiles are staged through LDS, both stored k-contiguous ("K-major"),
-//    BK floats per row, float4 slots XOR-swizzled by the row index so that the
-//    16-byte LDS writes and the MFMA fragment reads are free of bank conflicts
-//    without padding (the page pads its A tile to 17 for the same purpose).
+//  * A and W tiles are staged through LDS in their global orientation: A
+//    k-contiguous with its float4 slots XOR-swizzled by row, W n-contiguous
+//    with rows padded by four floats; both keep the 16-byte LDS writes and the
+//    MFMA fragment reads free of bank conflicts (the page pads its A tile to
+//    17 for the same purpose).  Binary16 weights are widened to fp32 and the
+//    SwiGLU combine silu(g) * u is applied to A on the way into LDS, so the
+//    LDS tiles always hold the exact fp32 operands.
 //  * Global loads are 16-byte (8-byte for four binary16 weights) and
-//    coalesced along the contiguous dimension.  The W tile is transposed in
-//    registers (4 x 4 blocks) on its way into LDS; binary16 weights are widened
-//    to fp32 there, and the SwiGLU combine silu(g) * u is applied to A there,
-//    so the LDS tiles always hold the exact fp32 operands.
+//    coalesced along the contiguous dimension.
+//  * On gfx950 fp32 MFMA and VALU work do not overlap on a SIMD, so staging
+//    is kept nearly free of VALU work: fp32 W is a plain copy, W16 costs one
+//    conversion per element, A costs nothing beyond the SwiGLU combine.
 //  * Two LDS stages, register prefetch: the loads for stage s+1 are issued
 //    before the MFMAs of stage s and written to the other stage after them;
 //    one barrier per stage (the page's "Çift Arabelleğe Alma").
@@ -35,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gemm_fwd.h"
 
@@ -98,34 +103,77 @@ __device__ __forceinline__ void tile_coords(const Params &p, int &tm, int &tn) {
 // the kernel
 // ---------------------------------------------------------------------------
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int MINB_>
+// Buffer resource over [base, base + bytes): loads at an offset >= bytes
+// return zeros without touching memory.  Masked elements (rows >= M, k >= K,
+// columns >= N) are loaded at kOOB, which is past every resource's end, so
+// the loads need no branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kOOB = (int)0x80000000u;
+
+// The base and size are the same in every lane; readfirstlane states that to
+// the compiler so the descriptor lives in scalar registers.
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    void *ub = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ f32x4 load_f32x4(Rsrc r, int off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+
+// Tile configuration.  WM x WN x WK "compute" waves own the MFMAs (WM x WN
+// wave tiles, K slices split over WK waves).  NP == 0: the same waves also
+// stage the operands (cooperative pipeline).  NP > 0: NP further waves do
+// all the staging (global loads, SwiGLU combine, f16 widening, LDS stores)
+// while the compute waves only read LDS and issue MFMAs, so the two kinds of
+// work overlap on every SIMD (specialised pipeline).  PF: K-stages of loads
+// in flight per staging thread (1 or 2).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int WM = WM_, WN = WN_, WK = WK_;  // waves along M, N, K
-    static constexpr int NT = 64 * WM * WN * WK;
-    static constexpr int MINB = MINB_;                  // workgroups per CU hint
+    static constexpr int WM = WM_, WN = WN_, WK = WK_;
+    static constexpr int NP = NP_, PF = PF_, MINB = MINB_;
+    static constexpr int NC = 64 * WM * WN * WK;        // compute threads
+    static constexpr int NS = NP > 0 ? 64 * NP : NC;    // staging threads
+    static constexpr int NT = NC + 64 * NP;             // block size
 };
 
-template <bool W16> struct BRegs;
-template <> struct BRegs<false> { f32x4 v[4]; };
-template <> struct BRegs<true> { f16x4 v[4]; };
+// Registers holding one K-stage of A (and UP) and W between its global load
+// and its LDS store.  Each W item is four consecutive columns of one row.
+template <int A_IT, int B_IT, bool SWIGLU, bool W16>
+struct StageRegs {
+    f32x4 a[A_IT];
+    f32x4 u[SWIGLU ? A_IT : 1];
+    typename std::conditional<W16, f16x4, f32x4>::type b[B_IT];
+};
 
 template <class C, bool SWIGLU, bool W16, bool RESID>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK;
-    constexpr int WM = C::WM, WN = C::WN, WK = C::WK, NT = C::NT;
+    constexpr int WM = C::WM, WN = C::WN, WK = C::WK;
+    constexpr int NC = C::NC, NS = C::NS;
+    constexpr bool SPEC = C::NP > 0;
     constexpr int SL = BK / 4;              // float4 slots per LDS row
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 16, TN = WTN / 16;
     constexpr int CH = BK / 16;             // 16-wide k slices per stage
     constexpr int A_F4 = BM * SL;           // float4s of A per stage
-    constexpr int A_IT = (A_F4 + NT - 1) / NT;
-    constexpr int NQ = BN / 4;
-    constexpr int B_MB = (BK / 4) * NQ;     // 4x4 blocks of W per stage
-    constexpr int B_IT = (B_MB + NT - 1) / NT;
-    constexpr int STAGE = (BM + BN) * BK;   // floats per LDS stage
+    constexpr int A_IT = (A_F4 + NS - 1) / NS;
+    constexpr int NQ = BN / 4;              // float4s per W row in the tile
+    constexpr int B_MB = BK * NQ;           // W items (row x 4 columns) per stage
+    constexpr int B_IT = (B_MB + NS - 1) / NS;
+    constexpr int BSTR = BN + 4;            // padded LDS row of the W tile (floats)
+    constexpr int STAGE = BM * BK + BK * BSTR;  // floats per LDS stage
     constexpr int RED = (WK - 1) * BM * BN; // floats for the K-split reduction
     constexpr int LDS_FLOATS = (2 * STAGE > RED) ? 2 * STAGE : RED;
+    constexpr int WBYTES = W16 ? 2 : 4;
     static_assert(BK % 32 == 0, "swizzle needs at least 8 slots per row");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be MFMA tiles");
     static_assert(CH % WK == 0, "K slices must split evenly over waves");
@@ -134,7 +182,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform role: compute waves first, then staging-only waves
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool computes = wave < WM * WN * WK;
+    const bool stages = SPEC ? !computes : true;
+    const int stid = SPEC ? tid - NC : tid;  // index among staging threads
     const int wk = wave % WK;
     const int wmn = wave / WK;
     const int wm = wmn / WN, wn = wmn % WN;
@@ -144,79 +196,85 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, K = p.K, N = p.N;
 
-    const float *Atile = p.A + (size_t)m0 * K;
-    const float *Utile = SWIGLU ? p.U + (size_t)m0 * K : nullptr;
+    // A (and UP) resources span the tile's valid rows, so rows >= M read as 0.
+    const int rows_valid = min(BM, M - m0);
+    const Rsrc rA = make_rsrc(p.A + (size_t)m0 * K, rows_valid * K * 4);
+    const Rsrc rU = SWIGLU ? make_rsrc(p.U + (size_t)m0 * K, rows_valid * K * 4) : rA;
+    const char *Wbase = static_cast<const char *>(p.W) + (size_t)n0 * WBYTES;
 
-    f32x4 ra[A_IT];
-    f32x4 ru[SWIGLU ? A_IT : 1];
-    BRegs<W16> rb[B_IT];
+    // Per-thread staging coordinates (fixed over the K loop).
+    int a_off[A_IT], a_gk[A_IT];
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+        const int f = stid + i * NS;
+        const int row = f / SL, slot = f % SL;
+        a_gk[i] = (A_IT * NS == A_F4 || f < A_F4) ? slot * 4 : K;  // out-of-range f: always masked
+        a_off[i] = (row * K + slot * 4) * 4;
+    }
+    // W items: consecutive staging threads take consecutive 4-column groups
+    // of a row, so each load instruction reads contiguous memory.
+    int b_off[B_IT], b_k[B_IT];
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+        const int mb = stid + i * NS;
+        const int k = mb / NQ, nq = mb % NQ;
+        const bool live = (B_IT * NS == B_MB || mb < B_MB) && (n0 + nq * 4 < N);
+        b_k[i] = live ? k : K;  // dead items are always masked
+        b_off[i] = (k * N + nq * 4) * WBYTES;
+    }
 
-    auto load_stage = [&](int k0) {
+    typedef StageRegs<A_IT, B_IT, SWIGLU, W16> Regs;
+
+    auto load_stage = [&](Regs &r, int k0) {
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
-            const int f = tid + i * NT;
-            const int row = f / SL, slot = f % SL;
-            const int gk = k0 + slot * 4;
-            const bool ok = (A_IT * NT == A_F4 || f < A_F4) && (m0 + row < M) && (gk < K);
-            const int off = row * K + gk;
-            ra[i] = ok ? *reinterpret_cast<const f32x4 *>(Atile + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (SWIGLU)
-                ru[i] = ok ? *reinterpret_cast<const f32x4 *>(Utile + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int off = (a_gk[i] + k0 < K) ? a_off[i] + k0 * 4 : kOOB;
+            r.a[i] = load_f32x4(rA, off);
+            if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, off);
         }
+        // W rows k0 .. k0+BK-1 from a resource based at row k0, so offsets stay
+        // 32-bit whatever K * N is.
+        const int krem = K - k0;
+        const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
+                                  krem > 0 ? min(krem, BK) * N * WBYTES : 0);
 #pragma unroll
         for (int i = 0; i < B_IT; ++i) {
-            const int mb = tid + i * NT;
-            const int kq = mb / NQ, nq = mb % NQ;
-            const int gk = k0 + kq * 4, gn = n0 + nq * 4;
-            const bool ok = (B_IT * NT == B_MB || mb < B_MB) && (gk < K) && (gn < N);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t off = (size_t)(gk + j) * N + gn;
-                if constexpr (W16) {
-                    rb[i].v[j] = ok ? *reinterpret_cast<const f16x4 *>(static_cast<const _Float16 *>(p.W) + off)
-                                    : f16x4{0, 0, 0, 0};
-                } else {
-                    rb[i].v[j] = ok ? *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.W) + off)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
+            const int voff = (b_k[i] < krem) ? b_off[i] : kOOB;
+            if constexpr (W16) r.b[i] = load_f16x4(rW, voff);
+            else r.b[i] = load_f32x4(rW, voff);
         }
     };
 
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](const Regs &r, int buf) {
         float *As = lds + buf * STAGE;
         float *Bs = As + BM * BK;
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
-            const int f = tid + i * NT;
-            if (A_IT * NT != A_F4 && f >= A_F4) continue;
+            const int f = stid + i * NS;
+            if (A_IT * NS != A_F4 && f >= A_F4) continue;
             const int row = f / SL, slot = f % SL;
-            f32x4 v = ra[i];
+            f32x4 v = r.a[i];
             if constexpr (SWIGLU) {
-                v.x = silu_mul(v.x, ru[i].x);
-                v.y = silu_mul(v.y, ru[i].y);
-                v.z = silu_mul(v.z, ru[i].z);
-                v.w = silu_mul(v.w, ru[i].w);
+                v.x = silu_mul(v.x, r.u[i].x);
+                v.y = silu_mul(v.y, r.u[i].y);
+                v.z = silu_mul(v.z, r.u[i].z);
+                v.w = silu_mul(v.w, r.u[i].w);
             }
             *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
         }
 #pragma unroll
         for (int i = 0; i < B_IT; ++i) {
-            const int mb = tid + i * NT;
-            if (B_IT * NT != B_MB && mb >= B_MB) continue;
-            const int kq = mb / NQ, nq = mb % NQ;
-            float w[4][4];  // w[j][c] = W[4kq + j][4nq + c]
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) w[j][c] = static_cast<float>(rb[i].v[j][c]);
+            const int mb = stid + i * NS;
+            if (B_IT * NS != B_MB && mb >= B_MB) continue;
+            const int k = mb / NQ, nq = mb % NQ;
+            f32x4 t;
+            if constexpr (W16) {
+                t = f32x4{static_cast<float>(r.b[i][0]), static_cast<float>(r.b[i][1]),
+                          static_cast<float>(r.b[i][2]), static_cast<float>(r.b[i][3])};
+            } else {
+                t = r.b[i];
             }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int n = nq * 4 + c;
-                const f32x4 t = {w[0][c], w[1][c], w[2][c], w[3][c]};
-                *reinterpret_cast<f32x4 *>(Bs + (n * SL + (kq ^ swz(n))) * 4) = t;
-            }
+            *reinterpret_cast<f32x4 *>(Bs + k * BSTR + nq * 4) = t;
         }
     };
 
@@ -239,10 +297,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 const int row = wm * WTM + i * 16 + r16;
                 af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4);
             }
+            // W is N-major in LDS: the four k of a lane are four rows; the row
+            // padding puts rows k and k+4 sixteen banks apart.
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = wn * WTN + j * 16 + r16;
-                bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (col * SL + (slot ^ swz(col))) * 4);
+                const float *b = Bs + (c * 16 + q4 * 4) * BSTR + wn * WTN + j * 16 + r16;
+                bf[j] = f32x4{b[0], b[BSTR], b[2 * BSTR], b[3 * BSTR]};
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -254,27 +314,107 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         }
     };
 
+    // K loop over nstages stages of BK, LDS double-buffered, one barrier per
+    // stage.  Loads past K are issued at kOOB and return zeros, so no stage
+    // needs a branch on its position.
+    //  PF == 2: two stages of loads in flight per staging thread: while stage
+    //   s is multiplied out of one LDS buffer, stage s+1 waits in registers
+    //   for the other buffer and stage s+2 is being fetched.
+    //  PF == 1: the loads of stage s+1 overlap the MFMAs of stage s.
     const int nstages = (K + BK - 1) / BK;
-    if (nstages > 0) {
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-        for (int s = 0; s < nstages; ++s) {
-            const bool more = s + 1 < nstages;
-            if (more) load_stage((s + 1) * BK);
-            compute_stage(s & 1);
-            if (more) store_stage((s + 1) & 1);
+
+    if constexpr (SPEC) {
+        // Staging waves run their own loop, one stage ahead of the compute
+        // waves, and meet them at the same barriers (equal counts on both
+        // sides, including the K-split reduction's).  Keeping the two loops
+        // apart lets the staging registers and the accumulators share VGPRs.
+        if (stages) {
+            if (nstages > 0) {
+                if constexpr (C::PF == 2) {
+                    Regs r0, r1;
+                    load_stage(r0, 0);
+                    load_stage(r1, BK);
+                    store_stage(r0, 0);
+                    load_stage(r0, 2 * BK);
+                    __syncthreads();
+                    for (int s = 0;; s += 2) {
+                        store_stage(r1, 1);
+                        load_stage(r1, (s + 3) * BK);
+                        __syncthreads();
+                        if (s + 1 >= nstages) break;
+                        store_stage(r0, 0);
+                        load_stage(r0, (s + 4) * BK);
+                        __syncthreads();
+                        if (s + 2 >= nstages) break;
+                    }
+                } else {
+                    Regs r0;
+                    load_stage(r0, 0);
+                    store_stage(r0, 0);
+                    load_stage(r0, BK);
+                    __syncthreads();
+                    for (int s = 0;; ++s) {
+                        store_stage(r0, (s + 1) & 1);
+                        load_stage(r0, (s + 2) * BK);
+                        __syncthreads();
+                        if (s + 1 >= nstages) break;
+                    }
+                }
+            }
+            if constexpr (WK > 1) __syncthreads();
+            return;
+        }
+        if (nstages > 0) {
             __syncthreads();
+            for (int s = 0;; ++s) {
+                compute_stage(s & 1);
+                __syncthreads();
+                if (s + 1 >= nstages) break;
+            }
+        }
+    } else if (nstages > 0) {
+        if constexpr (C::PF == 2) {
+            Regs r0, r1;
+            load_stage(r0, 0);
+            load_stage(r1, BK);
+            store_stage(r0, 0);
+            __syncthreads();
+            for (int s = 0;; s += 2) {
+                load_stage(r0, (s + 2) * BK);
+                compute_stage(0);
+                store_stage(r1, 1);
+                __syncthreads();
+                if (s + 1 >= nstages) break;
+                load_stage(r1, (s + 3) * BK);
+                compute_stage(1);
+                store_stage(r0, 0);
+                __syncthreads();
+                if (s + 2 >= nstages) break;
+            }
+        } else {
+            Regs r0;
+            load_stage(r0, 0);
+            store_stage(r0, 0);
+            __syncthreads();
+            for (int s = 0;; ++s) {
+                load_stage(r0, (s + 1) * BK);
+                compute_stage(s & 1);
+                if (s + 1 >= nstages) break;
+                store_stage(r0, (s + 1) & 1);
+                __syncthreads();
+            }
+            // the last stage was read without a closing barrier
+            if constexpr (WK > 1) __syncthreads();
         }
     }
 
     if constexpr (WK > 1) {
-        // Waves 1..WK-1 of each (wm, wn) park their partial tiles in LDS (the
-        // last barrier of the K loop has retired every read of the stages);
-        // wave 0 adds them in the fixed order 1, 2, ..., WK-1.
+        // Compute waves 1..WK-1 of each (wm, wn) park their partial tiles in
+        // LDS (the last barrier of the K loop has retired every read of the
+        // stages); wave 0 adds them in the fixed order 1, 2, ..., WK-1.
         f32x4 *red = reinterpret_cast<f32x4 *>(lds);
         constexpr int PART = TM * TN * 64;  // float4s per wave partial
-        if (wk > 0) {
+        if (computes && wk > 0) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -291,7 +431,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] += red[((w - 1) * WM * WN + wmn) * PART + (i * TN + j) * 64 + lane];
     }
-
     // Epilogue: lane holds rows 4*q4 .. 4*q4+3 of column r16 of each 16x16
     // MFMA tile.  Y = acc (+ R), masked to the matrix.
 #pragma unroll
@@ -340,23 +479,54 @@ constexpr ConfigEntry make_entry(const char *name) {
                          {gemm_fwd_kernel<C, true, true, false>, gemm_fwd_kernel<C, true, true, true>}}}};
 }
 
+//                      BM   BN   BK  WM WN WK NP PF MINB
 const ConfigEntry kConfigs[] = {
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 2>>("128x128x32_w2x2"),
-    make_entry<Tile<64, 64, 64, 2, 2, 1, 2>>("64x64x64_w2x2"),
-    make_entry<Tile<32, 48, 128, 1, 1, 4, 1>>("32x48x128_k4"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 1>>("64x48x64_w2x1_k2"),
+    // specialised: 4 staging waves beside the compute waves
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1>>("64x64x64_w2x2_sp4"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 4, 2, 1>>("64x96x64_w2x2_sp4"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1>>("64x48x64_w2x1_k2_sp4"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 2, 1>>("32x48x64_k4_sp4"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1>>("32x48x128_k4_sp4"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1>>("16x48x128_k4_sp4"),
+    make_entry<Tile<16, 96, 128, 1, 1, 4, 4, 2, 1>>("16x96x128_k4_sp4"),
+    // cooperative: every wave stages and computes
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 0, 1, 2>>("128x128x32_w2x2"),
+    make_entry<Tile<128, 128, 32, 2, 4, 1, 0, 1, 1>>("128x128x32_w2x4"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 0, 1, 2>>("64x64x64_w2x2"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 0, 2, 1>>("64x96x64_w2x2_pf2"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 0, 2, 2>>("32x48x64_k4_pf2"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 0, 2, 2>>("16x48x128_k4_pf2"),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int config_index(const char *name) {
+    for (int i = 0; i < kNumConfigs; ++i) {
+        const char *a = kConfigs[i].name, *b = name;
+        while (*a && *a == *b) ++a, ++b;
+        if (*a == 0 && *b == 0) return i;
+    }
+    return 0;
+}
+
+// Tile choice from the output grid, measured on MI355X: the largest tile
+// that still gives every CU at least two workgroups (a full second round),
+// then narrower tiles with the K range split over waves for small grids.
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
-    (void)K; (void)swiglu; (void)w16;
-    const int64_t big = ceil_div(M, 128) * ceil_div(N, 128);
-    if (big >= 256) return 0;
-    const int64_t mid = ceil_div(M, 64) * ceil_div(N, 64);
-    if (mid >= 192) return 1;
-    return 2;
+    (void)swiglu; (void)w16;
+    static const int big = config_index("128x128x32_w2x2_sp4");
+    static const int mid = config_index("64x64x64_w2x2_sp4");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp4");
+    static const int small = config_index("32x48x64_k4_sp4");
+    static const int deep = config_index("16x48x128_k4_sp4");
+    const int64_t cus = 256;
+    if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
+    if (ceil_div(M, 64) * ceil_div(N, 64) >= 2 * cus) return mid;
+    if (ceil_div(M, 64) * ceil_div(N, 48) >= cus) return narrow;
+    if (M <= 128 || K >= 2048) return deep;
+    return small;
 }
 
 // ---------------------------------------------------------------------------
@@ -382,9 +552,9 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
         (swiglu && ((mk && U == nullptr) || (mn && R == nullptr))))
         return GEMM_ERR_NULL;
     if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
-    // in-tile offsets (row * K + k, k * N + n within a stage) are 32-bit
-    if (K > 0 && 256 * K >= lim) return GEMM_ERR_SHAPE;
-    if (N > 0 && 256 * N >= lim) return GEMM_ERR_SHAPE;
+    // Buffer offsets are 32-bit: a tile's rows of A (up to 256 x K fp32) and a
+    // stage's rows of W (up to 128 x N fp32) must each stay below 2^31 bytes.
+    if (K * 1024 >= lim || N * 512 >= lim) return GEMM_ERR_SHAPE;
     if (config >= kNumConfigs) return GEMM_ERR_CONFIG;
     if ((A && !aligned(A, 16)) || (Y && !aligned(Y, 16)) || (U && !aligned(U, 16)) || (R && !aligned(R, 16)) ||
         (W && !aligned(W, w16 ? 8 : 16)))
