@@ -40,7 +40,7 @@
  *
  * Preconditions (the page's host-side rule that K and N be multiples of 4 for
  * the 16-byte vector loads, "Önemli Optimizasyonlar" §1):
- *   0 <= M < 2^31;  0 <= K < 2^21;  0 <= N < 2^22;  K % 4 == 0;  N % 4 == 0;
+ *   0 <= M < 2^31;  0 <= K < 2^21;  0 <= N < 2^21;  K % 4 == 0;  N % 4 == 0;
  *   fp32 arrays 16-byte aligned; binary16 W 8-byte aligned;
  *   Y overlaps none of the inputs (R included).
  * Degenerate shapes: M == 0 or N == 0 enqueues nothing and returns GEMM_OK;

@@ -124,6 +124,13 @@ __device__ __forceinline__ f32x4 load_f32x4(Rsrc r, int off) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+typedef unsigned int u32x4v __attribute__((vector_size(16)));
+
+// Out-of-range stores (offset >= resource size) are dropped by the hardware.
+__device__ __forceinline__ void store_f32x4(Rsrc r, int off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, 0);
+}
+
 __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
     return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
 }
@@ -171,8 +178,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int B_IT = (B_MB + NS - 1) / NS;
     constexpr int BSTR = BN + 4;            // padded LDS row of the W tile (floats)
     constexpr int STAGE = BM * BK + BK * BSTR;  // floats per LDS stage
-    constexpr int RED = (WK - 1) * BM * BN; // floats for the K-split reduction
-    constexpr int LDS_FLOATS = (2 * STAGE > RED) ? 2 * STAGE : RED;
+    constexpr int CSTR = BN + 4;            // padded row of the output tile in LDS
+    constexpr int CTILE = WK * BM * CSTR;   // floats for the output tile(s) in LDS
+    constexpr int LDS_FLOATS = (2 * STAGE > CTILE) ? 2 * STAGE : CTILE;
     constexpr int WBYTES = W16 ? 2 : 4;
     static_assert(BK % 32 == 0, "swizzle needs at least 8 slots per row");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be MFMA tiles");
@@ -330,7 +338,37 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         // apart lets the staging registers and the accumulators share VGPRs.
         if (stages) {
             if (nstages > 0) {
-                if constexpr (C::PF == 2) {
+                if constexpr (C::PF == 3) {
+                    // Three register sets: each step first issues the loads
+                    // of stage s+3, then combines and stores stage s+1, so
+                    // the address unit drains while the VALU works.
+                    Regs r0, r1, r2;
+                    load_stage(r0, 0);
+                    load_stage(r1, BK);
+                    load_stage(r2, 2 * BK);
+                    store_stage(r0, 0);
+                    __syncthreads();
+                    int s = 0;
+                    for (; s + 3 <= nstages; s += 3) {
+                        load_stage(r0, (s + 3) * BK);
+                        store_stage(r1, (s + 1) & 1);
+                        __syncthreads();
+                        load_stage(r1, (s + 4) * BK);
+                        store_stage(r2, (s + 2) & 1);
+                        __syncthreads();
+                        load_stage(r2, (s + 5) * BK);
+                        store_stage(r0, (s + 3) & 1);
+                        __syncthreads();
+                    }
+                    if (s < nstages) {
+                        store_stage(r1, (s + 1) & 1);
+                        __syncthreads();
+                    }
+                    if (s + 1 < nstages) {
+                        store_stage(r2, (s + 2) & 1);
+                        __syncthreads();
+                    }
+                } else if constexpr (C::PF == 2) {
                     Regs r0, r1;
                     load_stage(r0, 0);
                     load_stage(r1, BK);
@@ -361,7 +399,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     }
                 }
             }
-            if constexpr (WK > 1) __syncthreads();
+            __syncthreads();  // the epilogue's barrier
             return;
         }
         if (nstages > 0) {
@@ -404,51 +442,50 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 __syncthreads();
             }
             // the last stage was read without a closing barrier
-            if constexpr (WK > 1) __syncthreads();
+            __syncthreads();
         }
     }
 
-    if constexpr (WK > 1) {
-        // Compute waves 1..WK-1 of each (wm, wn) park their partial tiles in
-        // LDS (the last barrier of the K loop has retired every read of the
-        // stages); wave 0 adds them in the fixed order 1, 2, ..., WK-1.
-        f32x4 *red = reinterpret_cast<f32x4 *>(lds);
-        constexpr int PART = TM * TN * 64;  // float4s per wave partial
-        if (computes && wk > 0) {
+    // Epilogue through LDS (every K loop above ends with a barrier after its
+    // last read of the stages).  Each compute wave parks its accumulators in
+    // a padded row-major copy of the output tile, one copy per K-slice wave;
+    // then every compute thread takes whole float4s of the tile, adds the
+    // K-slice copies in the fixed order 0, 1, ..., WK-1, adds R, and stores
+    // Y with 16-byte buffer accesses.  Lane (q4, r16) of a 16x16 MFMA tile
+    // holds rows 4*q4 .. 4*q4+3 of column r16.
+    if (computes) {
+        float *Ct = lds + wk * BM * CSTR;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    red[((wk - 1) * WM * WN + wmn) * PART + (i * TN + j) * 64 + lane] = acc[i][j];
-        }
-        __syncthreads();
-        if (wk != 0) return;
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Ct[(wm * WTM + i * 16 + q4 * 4 + r) * CSTR + wn * WTN + j * 16 + r16] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (!computes) return;
+
+    const size_t tile_off = (size_t)m0 * N + n0;
+    const int64_t left = (int64_t)M * N - (int64_t)tile_off;  // elements from the tile origin
+    const int ybytes = (int)min<int64_t>(left * 4, 0x7fffffff);
+    const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
+    const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
+    constexpr int Q = BN / 4;
+    constexpr int ITEMS = BM * Q;
+#pragma unroll
+    for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
+        const int idx = tid + it * NC;
+        if (ITEMS % NC != 0 && idx >= ITEMS) break;
+        const int row = idx / Q, c4 = idx % Q;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(lds + row * CSTR + c4 * 4);
 #pragma unroll
         for (int w = 1; w < WK; ++w)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] += red[((w - 1) * WM * WN + wmn) * PART + (i * TN + j) * 64 + lane];
-    }
-    // Epilogue: lane holds rows 4*q4 .. 4*q4+3 of column r16 of each 16x16
-    // MFMA tile.  Y = acc (+ R), masked to the matrix.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + r16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * WTM + i * 16 + q4 * 4 + r;
-                if (row < M && col < N) {
-                    const size_t off = (size_t)row * N + col;
-                    float v = acc[i][j][r];
-                    if constexpr (RESID) v += p.R[off];
-                    p.Y[off] = v;
-                }
-            }
-        }
+            v += *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * CSTR + c4 * 4);
+        const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
+        const int off = ok ? (row * N + c4 * 4) * 4 : kOOB;
+        if constexpr (RESID) v += load_f32x4(rR, off);
+        store_f32x4(rY, off, v);
     }
 }
 
@@ -490,6 +527,14 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1>>("32x48x128_k4_sp4"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1>>("16x48x128_k4_sp4"),
     make_entry<Tile<16, 96, 128, 1, 1, 4, 4, 2, 1>>("16x96x128_k4_sp4"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1>>("128x128x32_w2x2_sp4_pf3"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 3, 1>>("64x64x64_w2x2_sp4_pf3"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1>>("64x48x64_w2x1_k2_sp4_pf3"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1>>("32x48x64_k4_sp4_pf3"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1>>("16x48x128_k4_sp4_pf3"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 4, 3, 1>>("16x96x64_k4_sp4_pf3"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 4, 2, 1>>("128x192x32_w2x2_sp4"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 4, 3, 1>>("32x96x64_w1x2_k2_sp4_pf3"),
     // cooperative: every wave stages and computes
     make_entry<Tile<128, 128, 32, 2, 2, 1, 0, 1, 2>>("128x128x32_w2x2"),
     make_entry<Tile<128, 128, 32, 2, 4, 1, 0, 1, 1>>("128x128x32_w2x4"),
@@ -512,20 +557,24 @@ int config_index(const char *name) {
 }
 
 // Tile choice from the output grid, measured on MI355X: the largest tile
-// that still gives every CU at least two workgroups (a full second round),
-// then narrower tiles with the K range split over waves for small grids.
+// that still gives every CU work for the whole kernel, then narrower tiles
+// with the K range split over waves for small grids.
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     (void)swiglu; (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4");
+    static const int wide = config_index("128x192x32_w2x2_sp4");
     static const int mid = config_index("64x64x64_w2x2_sp4");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp4");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3");
     static const int small = config_index("32x48x64_k4_sp4");
-    static const int deep = config_index("16x48x128_k4_sp4");
+    static const int deep = config_index("16x96x64_k4_sp4_pf3");
+    static const int tiny = config_index("16x48x128_k4_sp4");
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
+    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
     if (ceil_div(M, 64) * ceil_div(N, 64) >= 2 * cus) return mid;
     if (ceil_div(M, 64) * ceil_div(N, 48) >= cus) return narrow;
-    if (M <= 128 || K >= 2048) return deep;
+    if (M <= 128) return tiny;
+    if (K >= 2048) return deep;
     return small;
 }
 
@@ -552,9 +601,10 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
         (swiglu && ((mk && U == nullptr) || (mn && R == nullptr))))
         return GEMM_ERR_NULL;
     if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
-    // Buffer offsets are 32-bit: a tile's rows of A (up to 256 x K fp32) and a
-    // stage's rows of W (up to 128 x N fp32) must each stay below 2^31 bytes.
-    if (K * 1024 >= lim || N * 512 >= lim) return GEMM_ERR_SHAPE;
+    // Buffer offsets are 32-bit: a tile's rows of A (up to 256 x K fp32), a
+    // stage's rows of W and a tile's rows of Y (up to 256 x N fp32) must each
+    // stay below 2^31 bytes.
+    if (K * 1024 >= lim || N * 1024 >= lim) return GEMM_ERR_SHAPE;
     if (config >= kNumConfigs) return GEMM_ERR_CONFIG;
     if ((A && !aligned(A, 16)) || (Y && !aligned(Y, 16)) || (U && !aligned(U, 16)) || (R && !aligned(R, 16)) ||
         (W && !aligned(W, w16 ? 8 : 16)))
