@@ -39,6 +39,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_fwd.h"
@@ -57,7 +58,23 @@ struct Params {
     int M, K, N;
     int tiles_m, tiles_n;
     int group_m;     // M-tiles per group in the tile order
+    int kchunk;      // K range of one split (a multiple of BK) when K is split
+    int region;      // split-K workspace region of this call
 };
+
+// Split-K workspace.  When a configuration splits K over KS workgroups per
+// output tile, each writes its fp32 partial tile into its own slot, then
+// bumps the tile's counter; the last to arrive adds the KS slots in the fixed
+// order 0..KS-1 (so results do not depend on arrival order), adds R, writes
+// Y and resets the counter.  Static storage, zero at load, so no call
+// allocates; calls rotate over kSkRegions regions, so up to that many
+// split-K calls may be in flight at once on one device.
+constexpr int kSkRegions = 4;
+constexpr int kSkMaxSplit = 8;
+constexpr int kSkMaxElems = 1 << 19;   // M * N limit for split-K calls
+constexpr int kSkMaxTiles = 4096;
+__device__ float g_sk_ws[kSkRegions][kSkMaxSplit][kSkMaxElems];
+__device__ unsigned g_sk_cnt[kSkRegions][kSkMaxTiles];
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -85,11 +102,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // 0..7 in turn; renumber so that XCD x owns the contiguous range
 // [x*q + min(x, r), ...) of the tile order, then walk that order in groups
 // of group_m M-tiles (M fastest inside a group) for L2 reuse.
-__device__ __forceinline__ void tile_coords(const Params &p, int &tm, int &tn) {
+// With KS > 1 the KS workgroups of one tile are consecutive in that order
+// (split fastest), so they also share an XCD.
+template <int KS>
+__device__ __forceinline__ void tile_coords(const Params &p, int &tm, int &tn, int &split) {
     const int nb = gridDim.x;
     const int b = blockIdx.x;
     const int q = nb >> 3, r = nb & 7, x = b & 7;
-    const int t = x * q + (x < r ? x : r) + (b >> 3);
+    const int tt = x * q + (x < r ? x : r) + (b >> 3);
+    split = tt % KS;
+    const int t = tt / KS;
     const int per_group = p.group_m * p.tiles_n;
     const int g = t / per_group;
     const int first_m = g * p.group_m;
@@ -131,6 +153,17 @@ __device__ __forceinline__ void store_f32x4(Rsrc r, int off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, 0);
 }
 
+// Device-coherent 16-byte accesses (the sc1 cache policy, as used for
+// agent-scope atomic loads and stores): written through to, and read from,
+// the level shared by all XCDs.  Used only for split-K partial tiles.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ void store_f32x4_coherent(Rsrc r, int off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 load_f32x4_coherent(Rsrc r, int off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+
 __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
     return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
 }
@@ -142,11 +175,14 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // while the compute waves only read LDS and issue MFMAs, so the two kinds of
 // work overlap on every SIMD (specialised pipeline).  PF: K-stages of loads
 // in flight per staging thread (1 or 2).
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
+          int KS_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WM = WM_, WN = WN_, WK = WK_;
     static constexpr int NP = NP_, PF = PF_, MINB = MINB_;
+    static constexpr bool IL = IL_ != 0;  // interleave staging loads with VALU/LDS work
+    static constexpr int KS = KS_;        // workgroups sharing one output tile's K range
     static constexpr int NC = 64 * WM * WN * WK;        // compute threads
     static constexpr int NS = NP > 0 ? 64 * NP : NC;    // staging threads
     static constexpr int NT = NC + 64 * NP;             // block size
@@ -199,10 +235,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     const int wmn = wave / WK;
     const int wm = wmn / WN, wn = wmn % WN;
 
-    int tm, tn;
-    tile_coords(p, tm, tn);
+    constexpr int KS = C::KS;
+    static_assert(KS >= 1 && KS <= kSkMaxSplit, "split count");
+    int tm, tn, split;
+    tile_coords<KS>(p, tm, tn, split);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, K = p.K, N = p.N;
+    // this workgroup's K range [kbeg, kend)
+    const int kbeg = KS > 1 ? split * p.kchunk : 0;
+    const int kend = KS > 1 ? min(K, kbeg + p.kchunk) : K;
 
     // A (and UP) resources span the tile's valid rows, so rows >= M read as 0.
     const int rows_valid = min(BM, M - m0);
@@ -236,13 +277,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     auto load_stage = [&](Regs &r, int k0) {
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
-            const int off = (a_gk[i] + k0 < K) ? a_off[i] + k0 * 4 : kOOB;
+            const int off = (a_gk[i] + k0 < kend) ? a_off[i] + k0 * 4 : kOOB;
             r.a[i] = load_f32x4(rA, off);
             if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, off);
         }
         // W rows k0 .. k0+BK-1 from a resource based at row k0, so offsets stay
         // 32-bit whatever K * N is.
-        const int krem = K - k0;
+        const int krem = kend - k0;
         const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
                                   krem > 0 ? min(krem, BK) * N * WBYTES : 0);
 #pragma unroll
@@ -322,6 +363,24 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         }
     };
 
+    // Scheduling hint for a staging step (loads of a later stage, then the
+    // combine and LDS stores of the next one): alternate one global load with
+    // a share of the VALU work and one LDS store, so the address unit drains
+    // while the VALU works instead of stalling the wave at issue.
+    auto interleave_hint = [&]() {
+        if constexpr (C::IL) {
+            constexpr int NLOAD = A_IT * (SWIGLU ? 2 : 1) + B_IT;
+            constexpr int NVALU = (SWIGLU ? 36 * A_IT : 0) + (W16 ? 4 * B_IT : 0) + 2 * (A_IT + B_IT);
+            constexpr int PER = (NVALU + NLOAD - 1) / NLOAD;
+#pragma unroll
+            for (int i = 0; i < NLOAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // global load
+                __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);    // LDS store
+            }
+        }
+    };
+
     // K loop over nstages stages of BK, LDS double-buffered, one barrier per
     // stage.  Loads past K are issued at kOOB and return zeros, so no stage
     // needs a branch on its position.
@@ -329,7 +388,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     //   s is multiplied out of one LDS buffer, stage s+1 waits in registers
     //   for the other buffer and stage s+2 is being fetched.
     //  PF == 1: the loads of stage s+1 overlap the MFMAs of stage s.
-    const int nstages = (K + BK - 1) / BK;
+    const int nstages = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
     if constexpr (SPEC) {
         // Staging waves run their own loop, one stage ahead of the compute
@@ -343,21 +402,24 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     // of stage s+3, then combines and stores stage s+1, so
                     // the address unit drains while the VALU works.
                     Regs r0, r1, r2;
-                    load_stage(r0, 0);
-                    load_stage(r1, BK);
-                    load_stage(r2, 2 * BK);
+                    load_stage(r0, kbeg + 0);
+                    load_stage(r1, kbeg + BK);
+                    load_stage(r2, kbeg + 2 * BK);
                     store_stage(r0, 0);
                     __syncthreads();
                     int s = 0;
                     for (; s + 3 <= nstages; s += 3) {
-                        load_stage(r0, (s + 3) * BK);
+                        load_stage(r0, kbeg + (s + 3) * BK);
                         store_stage(r1, (s + 1) & 1);
+                        interleave_hint();
                         __syncthreads();
-                        load_stage(r1, (s + 4) * BK);
+                        load_stage(r1, kbeg + (s + 4) * BK);
                         store_stage(r2, (s + 2) & 1);
+                        interleave_hint();
                         __syncthreads();
-                        load_stage(r2, (s + 5) * BK);
+                        load_stage(r2, kbeg + (s + 5) * BK);
                         store_stage(r0, (s + 3) & 1);
+                        interleave_hint();
                         __syncthreads();
                     }
                     if (s < nstages) {
@@ -370,36 +432,40 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     }
                 } else if constexpr (C::PF == 2) {
                     Regs r0, r1;
-                    load_stage(r0, 0);
-                    load_stage(r1, BK);
+                    load_stage(r0, kbeg + 0);
+                    load_stage(r1, kbeg + BK);
                     store_stage(r0, 0);
-                    load_stage(r0, 2 * BK);
+                    load_stage(r0, kbeg + 2 * BK);
                     __syncthreads();
                     for (int s = 0;; s += 2) {
                         store_stage(r1, 1);
-                        load_stage(r1, (s + 3) * BK);
+                        load_stage(r1, kbeg + (s + 3) * BK);
                         __syncthreads();
                         if (s + 1 >= nstages) break;
                         store_stage(r0, 0);
-                        load_stage(r0, (s + 4) * BK);
+                        load_stage(r0, kbeg + (s + 4) * BK);
                         __syncthreads();
                         if (s + 2 >= nstages) break;
                     }
                 } else {
                     Regs r0;
-                    load_stage(r0, 0);
+                    load_stage(r0, kbeg + 0);
                     store_stage(r0, 0);
-                    load_stage(r0, BK);
+                    load_stage(r0, kbeg + BK);
                     __syncthreads();
                     for (int s = 0;; ++s) {
                         store_stage(r0, (s + 1) & 1);
-                        load_stage(r0, (s + 2) * BK);
+                        load_stage(r0, kbeg + (s + 2) * BK);
                         __syncthreads();
                         if (s + 1 >= nstages) break;
                     }
                 }
             }
             __syncthreads();  // the epilogue's barrier
+            if constexpr (KS > 1) {
+                __syncthreads();  // partials stored
+                __syncthreads();  // arrival counted
+            }
             return;
         }
         if (nstages > 0) {
@@ -413,17 +479,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     } else if (nstages > 0) {
         if constexpr (C::PF == 2) {
             Regs r0, r1;
-            load_stage(r0, 0);
-            load_stage(r1, BK);
+            load_stage(r0, kbeg + 0);
+            load_stage(r1, kbeg + BK);
             store_stage(r0, 0);
             __syncthreads();
             for (int s = 0;; s += 2) {
-                load_stage(r0, (s + 2) * BK);
+                load_stage(r0, kbeg + (s + 2) * BK);
                 compute_stage(0);
                 store_stage(r1, 1);
                 __syncthreads();
                 if (s + 1 >= nstages) break;
-                load_stage(r1, (s + 3) * BK);
+                load_stage(r1, kbeg + (s + 3) * BK);
                 compute_stage(1);
                 store_stage(r0, 0);
                 __syncthreads();
@@ -431,11 +497,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             }
         } else {
             Regs r0;
-            load_stage(r0, 0);
+            load_stage(r0, kbeg + 0);
             store_stage(r0, 0);
             __syncthreads();
             for (int s = 0;; ++s) {
-                load_stage(r0, (s + 1) * BK);
+                load_stage(r0, kbeg + (s + 1) * BK);
                 compute_stage(s & 1);
                 if (s + 1 >= nstages) break;
                 store_stage(r0, (s + 1) & 1);
@@ -464,15 +530,73 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     Ct[(wm * WTM + i * 16 + q4 * 4 + r) * CSTR + wn * WTN + j * 16 + r16] = acc[i][j][r];
     }
     __syncthreads();
-    if (!computes) return;
 
     const size_t tile_off = (size_t)m0 * N + n0;
+    constexpr int Q = BN / 4;
+    constexpr int ITEMS = BM * Q;
+    if constexpr (KS > 1) {
+        // Publish this split's partial tile, then count the arrival.
+        __shared__ int sk_last;
+        const int tile_id = tm * p.tiles_n + tn;
+        float *const slot0 = &g_sk_ws[p.region][0][0];
+        if (computes) {
+            const Rsrc rP = make_rsrc(slot0 + (size_t)split * kSkMaxElems + tile_off,
+                                      (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
+#pragma unroll
+            for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
+                const int idx = tid + it * NC;
+                if (ITEMS % NC != 0 && idx >= ITEMS) break;
+                const int row = idx / Q, c4 = idx % Q;
+                f32x4 v = *reinterpret_cast<const f32x4 *>(lds + row * CSTR + c4 * 4);
+#pragma unroll
+                for (int w = 1; w < WK; ++w)
+                    v += *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * CSTR + c4 * 4);
+                const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
+                store_f32x4_coherent(rP, ok ? (row * N + c4 * 4) * 4 : kOOB, v);
+            }
+        }
+        // Every thread's coherent partial stores have completed before the
+        // barrier, so they are visible device-wide before the arrival count
+        // moves.  (A device-scope fence would write back and invalidate the
+        // whole L2 of the XCD instead.)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            sk_last = __hip_atomic_fetch_add(&g_sk_cnt[p.region][tile_id], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(KS - 1);
+        __syncthreads();
+        if (!sk_last || !computes) return;
+        if (tid == 0)
+            __hip_atomic_store(&g_sk_cnt[p.region][tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int left = (int)(((int64_t)M * N - (int64_t)tile_off) * 4);
+        const Rsrc rY = make_rsrc(p.Y + tile_off, left);
+        const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, left) : rY;
+#pragma unroll
+        for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
+            const int idx = tid + it * NC;
+            if (ITEMS % NC != 0 && idx >= ITEMS) break;
+            const int row = idx / Q, c4 = idx % Q;
+            const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
+            const int off = ok ? (row * N + c4 * 4) * 4 : kOOB;
+            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sp = 0; sp < KS; ++sp) {
+                const Rsrc rP = make_rsrc(slot0 + (size_t)sp * kSkMaxElems + tile_off,
+                                          (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
+                v += load_f32x4_coherent(rP, off);
+            }
+            if constexpr (RESID) v += load_f32x4(rR, off);
+            store_f32x4(rY, off, v);
+        }
+        return;
+    }
+    if (!computes) return;
+
     const int64_t left = (int64_t)M * N - (int64_t)tile_off;  // elements from the tile origin
     const int ybytes = (int)min<int64_t>(left * 4, 0x7fffffff);
     const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
     const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
-    constexpr int Q = BN / 4;
-    constexpr int ITEMS = BM * Q;
 #pragma unroll
     for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
         const int idx = tid + it * NC;
@@ -503,13 +627,13 @@ typedef void (*KernelFn)(Params);
 
 struct ConfigEntry {
     const char *name;
-    int bm, bn, nt;
+    int bm, bn, bk, nt, ks;
     KernelFn fn[2][2][2];  // [swiglu][w16][resid]
 };
 
 template <class C>
 constexpr ConfigEntry make_entry(const char *name) {
-    return ConfigEntry{name, C::BM, C::BN, C::NT,
+    return ConfigEntry{name, C::BM, C::BN, C::BK, C::NT, C::KS,
                        {{{gemm_fwd_kernel<C, false, false, false>, gemm_fwd_kernel<C, false, false, true>},
                          {gemm_fwd_kernel<C, false, true, false>, gemm_fwd_kernel<C, false, true, true>}},
                         {{gemm_fwd_kernel<C, true, false, false>, gemm_fwd_kernel<C, true, false, true>},
@@ -533,6 +657,31 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1>>("32x48x64_k4_sp4_pf3"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1>>("16x48x128_k4_sp4_pf3"),
     make_entry<Tile<16, 96, 64, 1, 1, 4, 4, 3, 1>>("16x96x64_k4_sp4_pf3"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 4, 3, 1, 1>>("16x96x64_k4_sp4_pf3_il"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1>>("16x96x64_k4_sp8_pf3"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 1>>("32x48x64_k4_sp4_pf3_il"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1>>("32x48x64_k4_sp8_pf3"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1>>("64x48x64_w2x1_k2_sp4_pf3_il"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1>>("64x48x64_w2x1_k2_sp8_pf3"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 2, 1>>("128x128x32_w2x2_sp8"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 2, 1>>("128x192x32_w2x2_sp8"),
+    make_entry<Tile<16, 96, 128, 1, 1, 4, 8, 3, 1, 1>>("16x96x128_k4_sp8_pf3_il"),
+    make_entry<Tile<16, 96, 128, 1, 1, 4, 8, 2, 1>>("16x96x128_k4_sp8_pf2"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 3, 1, 1>>("32x48x128_k4_sp8_pf3_il"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1>>("32x48x64_k4_sp8_pf3_il"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1, 1>>("64x48x64_w2x1_k2_sp8_pf3_il"),
+    make_entry<Tile<64, 48, 128, 2, 1, 2, 8, 3, 1, 1>>("64x48x128_w2x1_k2_sp8_pf3_il"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 3, 1, 1>>("128x192x32_w2x2_sp8_pf3_il"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 3, 1, 1>>("128x128x32_w2x2_sp8_pf3_il"),
+    // split K over several workgroups per tile (deterministic fixed-order reduction)
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4>>("64x96x64_w2x2_sp8_pf3_il_ks4"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 2>>("64x96x64_w2x2_sp8_pf3_il_ks2"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("16x96x64_k4_sp8_pf3_il_ks2"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("32x48x64_k4_sp8_pf3_il_ks2"),
+    make_entry<Tile<128, 96, 64, 2, 2, 1, 8, 2, 1, 0, 8>>("128x96x64_w2x2_sp8_ks8"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 4, 3, 1, 1, 4>>("64x96x64_w2x2_sp4_pf3_il_ks4"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 4, 2, 1>>("128x192x32_w2x2_sp4"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 4, 3, 1>>("32x96x64_w1x2_k2_sp4_pf3"),
     // cooperative: every wave stages and computes
@@ -546,6 +695,14 @@ const ConfigEntry kConfigs[] = {
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split-K calls use the static workspace: the whole M x N output must fit a
+// slot and every tile needs a counter.
+bool split_fits(const ConfigEntry &e, int64_t M, int64_t N) {
+    return M * N <= kSkMaxElems && ceil_div(M, e.bm) * ceil_div(N, e.bn) <= kSkMaxTiles;
+}
+
+std::atomic<unsigned> g_region_ticket{0};
 
 int config_index(const char *name) {
     for (int i = 0; i < kNumConfigs; ++i) {
@@ -562,11 +719,12 @@ int config_index(const char *name) {
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     (void)swiglu; (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4");
-    static const int wide = config_index("128x192x32_w2x2_sp4");
+    static const int wide = config_index("128x192x32_w2x2_sp8_pf3_il");
     static const int mid = config_index("64x64x64_w2x2_sp4");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3");
-    static const int small = config_index("32x48x64_k4_sp4");
-    static const int deep = config_index("16x96x64_k4_sp4_pf3");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp8_pf3");
+    static const int small = config_index("32x48x64_k4_sp4_pf3");
+    static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
+    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2");
     static const int tiny = config_index("16x48x128_k4_sp4");
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
@@ -574,7 +732,12 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     if (ceil_div(M, 64) * ceil_div(N, 64) >= 2 * cus) return mid;
     if (ceil_div(M, 64) * ceil_div(N, 48) >= cus) return narrow;
     if (M <= 128) return tiny;
-    if (K >= 2048) return deep;
+    if (K >= 2048) {
+        // long K on a small grid: split K in two when the workspace holds it
+        if (split_fits(kConfigs[deep_split], M, N) && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
+            return deep_split;
+        return deep;
+    }
     return small;
 }
 
@@ -625,13 +788,16 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
 
     const int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
     const ConfigEntry &e = kConfigs[cfg];
+    if (e.ks > 1 && !split_fits(e, M, N)) return GEMM_ERR_CONFIG;
     Params p;
     p.A = A; p.U = U; p.W = W; p.R = R; p.Y = Y;
     p.M = (int)M; p.K = (int)K; p.N = (int)N;
     p.tiles_m = (int)ceil_div(M, e.bm);
     p.tiles_n = (int)ceil_div(N, e.bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
-    const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n;
+    p.kchunk = (int)(ceil_div(ceil_div(K, e.ks), e.bk) * e.bk);
+    p.region = e.ks > 1 ? (int)(g_region_ticket.fetch_add(1u, std::memory_order_relaxed) % kSkRegions) : 0;
+    const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, p);
