@@ -20,6 +20,13 @@ launches in the timed region.
 
 The CPU baseline is the fp64 oracle, timed on whole steps of the same five
 products (repeated for at least --cpu-seconds), on this host's cores.
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+this script (FETCH_SIZE, then WRITE_SIZE) and two of its --copy-calibration
+mode (a plain device copy of a known size), turned into bytes per launch by
+--traffic-from and kept in profiles/lm_head_traffic.json together with the
+hash of the kernel source they were taken on; the bench line reports them only
+while that hash still matches.
 """
 from __future__ import annotations
 
@@ -49,7 +56,75 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of COPY_BYTES (for counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="turn the rocprofv3 counter runs under DIR (fetch/, write/, copy_fetch/, copy_write/) "
+                         "into " + os.path.relpath(TRAFFIC_FILE, ROOT) + " and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+STEP_KERNELS = 5          # launches per step, lm_head last
+
+
+def copy_calibration():
+    import torch
+    x = torch.ones(COPY_BYTES // 4, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes 5 times", flush=True)
+
+
+def _counter_rows(run_dir):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def traffic_from(base):
+    """HBM bytes per lm_head launch from FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the same counter reads for a copy of COPY_BYTES."""
+    import numpy as np
+
+    def copy_kib(run):
+        vals = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(base, run))
+                if "copy" in r["Kernel_Name"].lower()]
+        return float(np.median(vals))
+
+    def lm_head_kib(run):
+        rows = [r for r in _counter_rows(os.path.join(base, run)) if "gemm_fwd_kernel" in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        vals = [float(r["Counter_Value"]) for i, r in enumerate(rows) if i % STEP_KERNELS == STEP_KERNELS - 1]
+        return float(np.mean(vals)), len(vals)
+
+    f_scale = COPY_BYTES / (copy_kib("copy_fetch") * 1024)
+    w_scale = COPY_BYTES / (copy_kib("copy_write") * 1024)
+    fetch_kib, n_f = lm_head_kib("fetch")
+    write_kib, n_w = lm_head_kib("write")
+    fetch = fetch_kib * 1024 * f_scale
+    write = write_kib * 1024 * w_scale
+    out = {
+        "kernel_sha256_16": kernel_hash(),
+        "kernel": "lm_head (matmul_w16 512x768x16384)",
+        "bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "fetch_size_kib_raw": round(fetch_kib, 1), "write_size_kib_raw": round(write_kib, 1),
+        "copy_scale": {"FETCH_SIZE": round(f_scale, 4), "WRITE_SIZE": round(w_scale, 4)},
+        "algorithmic_bytes": 512 * 768 * 4 + 768 * 16384 * 2 + 512 * 16384 * 4,
+        "dispatches": {"fetch": n_f, "write": n_w},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def kernel_hash():
@@ -103,6 +178,12 @@ def cpu_baseline(cases, min_seconds):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args.traffic_from)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the GEMM shards by rows or columns with no exchange; see DESIGN.md)", file=sys.stderr)

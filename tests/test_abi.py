@@ -55,7 +55,9 @@ def test_config_table(lib):
     names = [lib.gemm_config_name(i).decode() for i in range(n)]
     assert len(set(names)) == n
     assert lib.gemm_config_name(n) is None and lib.gemm_config_name(-1) is None
-    for shape in [(512, 768, 16384), (512, 3072, 768), (128, 768, 768), (8192, 768, 50304), (1, 4, 4)]:
+    # one shape per branch of the library's tile choice
+    for shape in [(512, 768, 16384), (8192, 3072, 768), (1024, 768, 2048), (512, 768, 3072), (128, 768, 768),
+                  (512, 3072, 768), (256, 4096, 768), (512, 768, 768), (8192, 768, 50304), (1, 4, 4)]:
         for sw in (0, 1):
             for w16 in (0, 1):
                 assert 0 <= lib.gemm_select_config(*shape, sw, w16) < n

@@ -148,6 +148,7 @@ __device__ __forceinline__ f32x4 load_f32x4(Rsrc r, int off) {
 
 typedef unsigned int u32x4v __attribute__((vector_size(16)));
 
+
 // Out-of-range stores (offset >= resource size) are dropped by the hardware.
 __device__ __forceinline__ void store_f32x4(Rsrc r, int off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, 0);
@@ -176,8 +177,10 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // work overlap on every SIMD (specialised pipeline).  PF: K-stages of loads
 // in flight per staging thread (1 or 2).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
-          int KS_ = 1>
+          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2>
 struct Tile {
+    static constexpr bool CIL = CIL_ != 0;  // pipeline fragment reads one k-slice ahead of the MFMAs
+    static constexpr int PRIO = PRIO_;      // wave priority of the staging waves
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WM = WM_, WN = WN_, WK = WK_;
     static constexpr int NP = NP_, PF = PF_, MINB = MINB_;
@@ -361,6 +364,29 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][t], bf[j][t], acc[i][j], 0, 0, 0);
         }
+        if constexpr (C::CIL) {
+            // Scheduling hint: read all fragments of the first k-slice, then
+            // spread each later slice's reads over the MFMAs of the slice
+            // before it, so LDS latency hides behind matrix work instead of
+            // stalling in front of every few MFMAs.
+            constexpr int NCH = CH / WK;
+            constexpr int DS = TM + 2 * TN;     // b128 per A fragment, two read2_b32 per W fragment
+            constexpr int MF = 4 * TM * TN;
+            constexpr int PER = (MF + DS - 1) / DS;
+            __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (c + 1 < NCH) {
+#pragma unroll
+                    for (int d = 0; d < DS; ++d) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+                }
+            }
+        }
     };
 
     // Scheduling hint for a staging step (loads of a later stage, then the
@@ -396,6 +422,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         // sides, including the K-split reduction's).  Keeping the two loops
         // apart lets the staging registers and the accumulators share VGPRs.
         if (stages) {
+            // Staging waves outrank the compute wave of their SIMD, so their
+            // short VALU bursts slot in between MFMAs as soon as their data
+            // lands, instead of queueing behind a whole stage of MFMAs and
+            // holding the next barrier back.
+            __builtin_amdgcn_s_setprio(C::PRIO);
             if (nstages > 0) {
                 if constexpr (C::PF == 3) {
                     // Three register sets: each step first issues the loads
@@ -569,9 +600,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         if (!sk_last || !computes) return;
         if (tid == 0)
             __hip_atomic_store(&g_sk_cnt[p.region][tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int left = (int)(((int64_t)M * N - (int64_t)tile_off) * 4);
-        const Rsrc rY = make_rsrc(p.Y + tile_off, left);
-        const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, left) : rY;
+        const int ybytes = rows_valid * N * 4;
+        const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
+        const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
 #pragma unroll
         for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
             const int idx = tid + it * NC;
@@ -579,12 +610,22 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             const int row = idx / Q, c4 = idx % Q;
             const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
             const int off = ok ? (row * N + c4 * 4) * 4 : kOOB;
+            // this split's own partial is still in LDS; the others come from
+            // the workspace.  Summation order 0..KS-1 whatever arrived last.
+            f32x4 own = *reinterpret_cast<const f32x4 *>(lds + row * CSTR + c4 * 4);
+#pragma unroll
+            for (int w = 1; w < WK; ++w)
+                own += *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * CSTR + c4 * 4);
             f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sp = 0; sp < KS; ++sp) {
-                const Rsrc rP = make_rsrc(slot0 + (size_t)sp * kSkMaxElems + tile_off,
-                                          (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
-                v += load_f32x4_coherent(rP, off);
+                if (sp == split) {
+                    v += own;
+                } else {
+                    const Rsrc rP = make_rsrc(slot0 + (size_t)sp * kSkMaxElems + tile_off,
+                                              (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
+                    v += load_f32x4_coherent(rP, off);
+                }
             }
             if constexpr (RESID) v += load_f32x4(rR, off);
             store_f32x4(rY, off, v);
@@ -593,8 +634,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     }
     if (!computes) return;
 
-    const int64_t left = (int64_t)M * N - (int64_t)tile_off;  // elements from the tile origin
-    const int ybytes = (int)min<int64_t>(left * 4, 0x7fffffff);
+    // The tile's valid rows span rows_valid * N elements from its origin
+    // (under 2^30 bytes by the shape limits); masked items use kOOB.
+    const int ybytes = rows_valid * N * 4;
     const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
     const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
 #pragma unroll
@@ -640,53 +682,34 @@ constexpr ConfigEntry make_entry(const char *name) {
                          {gemm_fwd_kernel<C, true, true, false>, gemm_fwd_kernel<C, true, true, true>}}}};
 }
 
-//                      BM   BN   BK  WM WN WK NP PF MINB
+// Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL>: the configurations
+// that win on some shape of the forward family, plus one of each kind of
+// pipeline so that every code path stays built and tested.
 const ConfigEntry kConfigs[] = {
-    // specialised: 4 staging waves beside the compute waves
+    // specialised: NP staging waves beside the compute waves
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 1>>("128x128x32_w2x2_sp4_cil"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 2, 1>>("128x128x32_w2x2_sp8"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 3, 1, 1>>("128x192x32_w2x2_sp8_pf3_il"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 2, 1>>("128x192x32_w2x2_sp8"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1>>("64x64x64_w2x2_sp4"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 4, 2, 1>>("64x96x64_w2x2_sp4"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1>>("64x48x64_w2x1_k2_sp4"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 2, 1>>("32x48x64_k4_sp4"),
-    make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1>>("32x48x128_k4_sp4"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1>>("16x48x128_k4_sp4"),
-    make_entry<Tile<16, 96, 128, 1, 1, 4, 4, 2, 1>>("16x96x128_k4_sp4"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1>>("128x128x32_w2x2_sp4_pf3"),
-    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 3, 1>>("64x64x64_w2x2_sp4_pf3"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1>>("64x48x64_w2x1_k2_sp4_pf3"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1>>("32x48x64_k4_sp4_pf3"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1>>("16x48x128_k4_sp4_pf3"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 4, 3, 1>>("16x96x64_k4_sp4_pf3"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 4, 3, 1, 1>>("16x96x64_k4_sp4_pf3_il"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1>>("16x96x64_k4_sp8_pf3"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 1>>("32x48x64_k4_sp4_pf3_il"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1>>("32x48x64_k4_sp8_pf3"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1>>("64x48x64_w2x1_k2_sp4_pf3_il"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1>>("64x48x64_w2x1_k2_sp8_pf3"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 2, 1>>("128x128x32_w2x2_sp8"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 2, 1>>("128x192x32_w2x2_sp8"),
-    make_entry<Tile<16, 96, 128, 1, 1, 4, 8, 3, 1, 1>>("16x96x128_k4_sp8_pf3_il"),
-    make_entry<Tile<16, 96, 128, 1, 1, 4, 8, 2, 1>>("16x96x128_k4_sp8_pf2"),
-    make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 3, 1, 1>>("32x48x128_k4_sp8_pf3_il"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1>>("32x48x64_k4_sp8_pf3_il"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1, 1>>("64x48x64_w2x1_k2_sp8_pf3_il"),
-    make_entry<Tile<64, 48, 128, 2, 1, 2, 8, 3, 1, 1>>("64x48x128_w2x1_k2_sp8_pf3_il"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 3, 1, 1>>("128x192x32_w2x2_sp8_pf3_il"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 3, 1, 1>>("128x128x32_w2x2_sp8_pf3_il"),
-    // split K over several workgroups per tile (deterministic fixed-order reduction)
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4>>("64x96x64_w2x2_sp8_pf3_il_ks4"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 2>>("64x96x64_w2x2_sp8_pf3_il_ks2"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1>>("64x48x64_w2x1_k2_sp4_pf3_il"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1>>("32x48x64_k4_sp4_pf3"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1>>("32x48x64_k4_sp4_pf3_cil"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1>>("16x48x128_k4_sp4"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
+    // specialised with the K range split over KS workgroups
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("16x96x64_k4_sp8_pf3_il_ks2"),
+    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("32x48x64_k4_sp8_pf3_il_ks2"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("16x96x64_k4_sp8_pf3_il_ks2"),
     make_entry<Tile<128, 96, 64, 2, 2, 1, 8, 2, 1, 0, 8>>("128x96x64_w2x2_sp8_ks8"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 4, 3, 1, 1, 4>>("64x96x64_w2x2_sp4_pf3_il_ks4"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 4, 2, 1>>("128x192x32_w2x2_sp4"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 4, 3, 1>>("32x96x64_w1x2_k2_sp4_pf3"),
     // cooperative: every wave stages and computes
     make_entry<Tile<128, 128, 32, 2, 2, 1, 0, 1, 2>>("128x128x32_w2x2"),
-    make_entry<Tile<128, 128, 32, 2, 4, 1, 0, 1, 1>>("128x128x32_w2x4"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 0, 1, 2>>("64x64x64_w2x2"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 0, 2, 1>>("64x96x64_w2x2_pf2"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 0, 2, 2>>("32x48x64_k4_pf2"),
@@ -710,7 +733,7 @@ int config_index(const char *name) {
         while (*a && *a == *b) ++a, ++b;
         if (*a == 0 && *b == 0) return i;
     }
-    return 0;
+    return -1;
 }
 
 // Tile choice from the output grid, measured on MI355X: the largest tile
@@ -722,10 +745,15 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     static const int wide = config_index("128x192x32_w2x2_sp8_pf3_il");
     static const int mid = config_index("64x64x64_w2x2_sp4");
     static const int narrow = config_index("64x48x64_w2x1_k2_sp8_pf3");
-    static const int small = config_index("32x48x64_k4_sp4_pf3");
+    static const int small = config_index("32x48x64_k4_sp4_pf3_cil");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2");
+    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil");
     static const int tiny = config_index("16x48x128_k4_sp4");
+    // a name missing from the table is a build error in spirit: report it
+    // as an unavailable configuration rather than run another one
+    static const bool complete = big >= 0 && wide >= 0 && mid >= 0 && narrow >= 0 && small >= 0 &&
+                                 deep >= 0 && deep_split >= 0 && tiny >= 0;
+    if (!complete) return -1;
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
     if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
@@ -787,6 +815,7 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     }
 
     const int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
+    if (cfg < 0 || cfg >= kNumConfigs) return GEMM_ERR_CONFIG;
     const ConfigEntry &e = kConfigs[cfg];
     if (e.ks > 1 && !split_fits(e, M, N)) return GEMM_ERR_CONFIG;
     Params p;
