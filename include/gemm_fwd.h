@@ -26,17 +26,27 @@
  * on the matrix cores; binary16 weights are widened exactly to fp32 before use.
  *
  * Ownership.  All array pointers are device pointers owned by the caller.  The
- * library never allocates, frees or keeps device memory.  A call only enqueues
- * work on `stream` (a hipStream_t; NULL means the null stream) and returns;
- * inputs must stay valid and unmodified, and Y must not be read, until the
- * stream has passed the kernel.  Only Y[i][j] for i < M, j < N is written, and
- * nothing outside the inputs is read.  Results are bitwise reproducible from
- * run to run for the same inputs, shape and configuration.
+ * library never allocates or frees device memory.  A call only enqueues work
+ * on `stream` (a hipStream_t; NULL means the null stream) and returns; inputs
+ * must stay valid and unmodified, and Y must not be read, until the stream has
+ * passed the kernel.  Only Y[i][j] for i < M, j < N is written, and nothing
+ * outside the inputs is read.  Results are bitwise reproducible from run to
+ * run for the same inputs, shape and configuration.
+ *
+ * Split-K workspace.  For small output grids with a long K (M * N <= 2^19)
+ * the library may split K over several workgroups per output tile; their
+ * fp32 partial tiles meet in a static device workspace that the library
+ * holds for the life of the process (64 MiB plus 64 KiB of counters per
+ * device), so no call allocates.  Successive calls rotate over 4 regions of
+ * it: at most 4 such calls may be in flight at once on one device (calls on
+ * one stream never overlap; more than 4 streams running split-K calls
+ * concurrently would race).  The counters are left at zero by every call.
  *
  * Errors.  Arguments are validated synchronously before anything is enqueued;
  * on a negative status nothing is launched and Y is untouched.  No exception or
  * abort crosses this interface.  Calls may be made from several host threads;
- * the library has no mutable global state.
+ * the only mutable host state is an atomic counter that picks the workspace
+ * region.
  *
  * Preconditions (the page's host-side rule that K and N be multiples of 4 for
  * the 16-byte vector loads, "Önemli Optimizasyonlar" §1):
@@ -104,6 +114,22 @@ int gemm_fwd_cfg(const float *X, const void *W, const float *R, float *Y,
                  int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream);
 int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
                         int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream);
+
+/*
+ * Same as gemm_fwd_cfg / gemm_fwd_swiglu_cfg, and in addition the kernel's own
+ * start and end are recorded into `start` and `stop` (hipEvent_t handles
+ * created by the caller; either may be NULL).  Unlike hipEventRecord calls
+ * placed around an ordinary launch, these exclude the stream's dispatch
+ * latency, so hipEventElapsedTime(start, stop) is the kernel's run time.  For
+ * timing harnesses; nothing is recorded when the status is negative or when
+ * there is nothing to launch (M == 0 or N == 0).
+ */
+int gemm_fwd_timed(const float *X, const void *W, const float *R, float *Y,
+                   int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream,
+                   void *start, void *stop);
+int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                          int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream,
+                          void *start, void *stop);
 
 /* Number of tile configurations compiled into the library. */
 int gemm_num_configs(void);

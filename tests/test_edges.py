@@ -175,3 +175,39 @@ def test_aliased_output_is_rejected():
     import torch
     torch.cuda.synchronize()
     assert torch.equal(R, keep)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_timed_entry_points_match_and_record(swiglu):
+    """gemm_fwd_timed / gemm_fwd_swiglu_timed compute exactly what the plain
+    entry points compute (same configuration) and leave a positive kernel
+    time in the caller's events."""
+    import torch
+    b = _lib()
+    lib = b.load_library()
+    c = inputs.random_case(11, 200, 320, 136, swiglu=swiglu, w16=swiglu, residual=True)
+    say(f"timed entry point swiglu={swiglu} M=200 K=320 N=136")
+    W, R = to_dev(c["W"]), to_dev(c["R"])
+    M, K, N = 200, 320, 136
+    y0 = torch.empty((M, N), device=device())
+    y1 = torch.full((M, N), float("nan"), device=device())
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    e1.record(st)
+    if swiglu:
+        G, U = to_dev(c["G"]), to_dev(c["U"])
+        a = (G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr())
+        assert lib.gemm_fwd_swiglu(*a, y0.data_ptr(), M, K, N, 1, st.cuda_stream) == 0
+        assert lib.gemm_fwd_swiglu_timed(*a, y1.data_ptr(), M, K, N, 1, -1, st.cuda_stream,
+                                         e0.cuda_event, e1.cuda_event) == 0
+    else:
+        X = to_dev(c["X"])
+        a = (X.data_ptr(), W.data_ptr(), R.data_ptr())
+        assert lib.gemm_fwd(*a, y0.data_ptr(), M, K, N, 0, st.cuda_stream) == 0
+        assert lib.gemm_fwd_timed(*a, y1.data_ptr(), M, K, N, 0, -1, st.cuda_stream,
+                                  e0.cuda_event, e1.cuda_event) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    assert e0.elapsed_time(e1) > 0.0
+    check(c, y1.cpu().numpy(), label="timed")

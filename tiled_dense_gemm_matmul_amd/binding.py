@@ -53,6 +53,10 @@ def load_library():
     lib.gemm_fwd_cfg.restype = c_int
     lib.gemm_fwd_swiglu_cfg.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, c_int, p]
     lib.gemm_fwd_swiglu_cfg.restype = c_int
+    lib.gemm_fwd_timed.argtypes = [p, p, p, p, i64, i64, i64, u32, c_int, p, p, p]
+    lib.gemm_fwd_timed.restype = c_int
+    lib.gemm_fwd_swiglu_timed.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, c_int, p, p, p]
+    lib.gemm_fwd_swiglu_timed.restype = c_int
     lib.gemm_num_configs.argtypes = []
     lib.gemm_num_configs.restype = c_int
     lib.gemm_config_name.argtypes = [c_int]

@@ -5,9 +5,11 @@
 //   Y = A @ W (+ R),  A = X  or  A = silu(GATE) * UP,  W fp32 or binary16.
 //
 // Design (gfx950, wave64, fp32 matrix cores):
-//  * One workgroup owns one BM x BN output tile over the whole K range (the
-//    page's "Tile Hiyerarşisi"), so there are no atomics and no workspace and
-//    every run gives the same bits.
+//  * One workgroup owns one BM x BN output tile over its K range (the page's
+//    "Tile Hiyerarşisi").  On small output grids the K range of a tile is
+//    split over KS workgroups whose fp32 partial tiles meet in a static
+//    workspace and are added in the fixed order 0..KS-1, so every run gives
+//    the same bits whatever order the workgroups finish in.
 //  * The contraction runs on v_mfma_f32_16x16x4_f32.  Within a 16-wide slice
 //    of K each lane feeds four consecutive k values (one float4) to four
 //    MFMAs; the pairing of k with lanes is the same for A and B, so the sum
@@ -19,22 +21,25 @@
 //    17 for the same purpose).  Binary16 weights are widened to fp32 and the
 //    SwiGLU combine silu(g) * u is applied to A on the way into LDS, so the
 //    LDS tiles always hold the exact fp32 operands.
-//  * Global loads are 16-byte (8-byte for four binary16 weights) and
+//  * Global loads are 16-byte (8-byte for four binary16 weights) buffer loads,
 //    coalesced along the contiguous dimension.
-//  * On gfx950 fp32 MFMA and VALU work do not overlap on a SIMD, so staging
-//    is kept nearly free of VALU work: fp32 W is a plain copy, W16 costs one
-//    conversion per element, A costs nothing beyond the SwiGLU combine.
-//  * Two LDS stages, register prefetch: the loads for stage s+1 are issued
-//    before the MFMAs of stage s and written to the other stage after them;
-//    one barrier per stage (the page's "Çift Arabelleğe Alma").
-//  * Small output grids split K across the four waves of a workgroup; their
-//    partial tiles are added through LDS in a fixed order.
+//  * On gfx950 fp32 MFMA and VALU work do not overlap on a SIMD, so every
+//    VALU cycle of staging is taken from the MFMAs: fp32 W is a plain copy,
+//    W16 costs one conversion per element, A costs only the SwiGLU combine.
+//  * Specialised pipeline: staging waves (loads, combine, LDS writes, one to
+//    three K-stages of loads in flight) run beside compute waves (LDS reads
+//    and MFMAs only) at a higher wave priority, over two LDS stages with one
+//    barrier per stage (the page's "Çift Arabelleğe Alma").  Cooperative
+//    configurations, where every wave does both, remain for comparison.
+//  * Small output grids also split K across the compute waves of a
+//    workgroup; their partial tiles are added through LDS in a fixed order.
 //  * Workgroups are handed to the 8 XCDs round-robin; the tile order is
 //    renumbered so that each XCD works on a contiguous, M-grouped range of
 //    tiles and its private L2 sees reuse of both operands.
 //  * Edges: rows >= M, columns >= N and k >= K are staged as zeros and never
 //    read; stores are masked to i < M, j < N.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -782,7 +787,8 @@ bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, const float *R, float *Y,
-        int64_t M, int64_t K, int64_t N, int config, void *stream) {
+        int64_t M, int64_t K, int64_t N, int config, void *stream, void *start = nullptr,
+        void *stop = nullptr) {
     const int64_t lim = (int64_t)1 << 31;
     if (M < 0 || K < 0 || N < 0 || M >= lim || K >= lim || N >= lim) return GEMM_ERR_SHAPE;
     // A pointer may be NULL only when its array holds no element (an empty
@@ -810,7 +816,8 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0) {
         const int64_t count = M * N;
-        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, R, Y, count);
+        hipExtLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s,
+                              static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop), 0, R, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
 
@@ -829,7 +836,10 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, p);
+    // with NULL events this is a plain launch; otherwise the events take the
+    // kernel's own start and end times
+    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, static_cast<hipEvent_t>(start),
+                          static_cast<hipEvent_t>(stop), 0, p);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -847,6 +857,12 @@ int gemm_fwd(const float *X, const void *W, const float *R, float *Y,
              int64_t M, int64_t K, int64_t N, uint32_t flags, void *stream) {
     return gemm_fwd_cfg(X, W, R, Y, M, K, N, flags, -1, stream);
 }
+int gemm_fwd_timed(const float *X, const void *W, const float *R, float *Y, int64_t M, int64_t K, int64_t N,
+                   uint32_t flags, int config, void *stream, void *start, void *stop) {
+    if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
+    return run(false, X, nullptr, W, (flags & GEMM_FLAG_W_F16) != 0, R, Y, M, K, N, config, stream, start,
+               stop);
+}
 
 int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
                         int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream) {
@@ -857,6 +873,12 @@ int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const
 int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
                     int64_t M, int64_t K, int64_t N, int w_dtype, void *stream) {
     return gemm_fwd_swiglu_cfg(GATE, UP, W, R, Y, M, K, N, w_dtype, -1, stream);
+}
+int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                          int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream, void *start,
+                          void *stop) {
+    if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
+    return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, config, stream, start, stop);
 }
 
 int gemm_num_configs(void) { return kNumConfigs; }
