@@ -179,8 +179,8 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // stage the operands (cooperative pipeline).  NP > 0: NP further waves do
 // all the staging (global loads, SwiGLU combine, f16 widening, LDS stores)
 // while the compute waves only read LDS and issue MFMAs, so the two kinds of
-// work overlap on every SIMD (specialised pipeline).  PF: K-stages of loads
-// in flight per staging thread (1 or 2).
+// work overlap on every SIMD (specialised pipeline).  PF: register sets of
+// staged K-stages per staging thread (1 to 5); loads run PF-1 stages ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
           int KS_ = 1, int CIL_ = 0, int PRIO_ = 2>
 struct Tile {
@@ -433,38 +433,34 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             // holding the next barrier back.
             __builtin_amdgcn_s_setprio(C::PRIO);
             if (nstages > 0) {
-                if constexpr (C::PF == 3) {
-                    // Three register sets: each step first issues the loads
-                    // of stage s+3, then combines and stores stage s+1, so
-                    // the address unit drains while the VALU works.
-                    Regs r0, r1, r2;
-                    load_stage(r0, kbeg + 0);
-                    load_stage(r1, kbeg + BK);
-                    load_stage(r2, kbeg + 2 * BK);
-                    store_stage(r0, 0);
+                if constexpr (C::PF >= 3) {
+                    // PF register sets, stage t in set t % PF: each step
+                    // first issues the loads of stage s+PF into the set just
+                    // stored, then combines and stores stage s+1, so the
+                    // address unit drains while the VALU works and every
+                    // load has PF-1 steps to land.
+                    constexpr int PF = C::PF;
+                    Regs r[PF];
+#pragma unroll
+                    for (int j = 0; j < PF; ++j) load_stage(r[j], kbeg + j * BK);
+                    store_stage(r[0], 0);
                     __syncthreads();
                     int s = 0;
-                    for (; s + 3 <= nstages; s += 3) {
-                        load_stage(r0, kbeg + (s + 3) * BK);
-                        store_stage(r1, (s + 1) & 1);
-                        interleave_hint();
-                        __syncthreads();
-                        load_stage(r1, kbeg + (s + 4) * BK);
-                        store_stage(r2, (s + 2) & 1);
-                        interleave_hint();
-                        __syncthreads();
-                        load_stage(r2, kbeg + (s + 5) * BK);
-                        store_stage(r0, (s + 3) & 1);
-                        interleave_hint();
-                        __syncthreads();
+                    for (; s + PF <= nstages; s += PF) {
+#pragma unroll
+                        for (int j = 0; j < PF; ++j) {
+                            load_stage(r[j], kbeg + (s + j + PF) * BK);
+                            store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
+                            interleave_hint();
+                            __syncthreads();
+                        }
                     }
-                    if (s < nstages) {
-                        store_stage(r1, (s + 1) & 1);
-                        __syncthreads();
-                    }
-                    if (s + 1 < nstages) {
-                        store_stage(r2, (s + 2) & 1);
-                        __syncthreads();
+#pragma unroll
+                    for (int j = 0; j + 1 < PF; ++j) {
+                        if (s + j < nstages) {
+                            store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
+                            __syncthreads();
+                        }
                     }
                 } else if constexpr (C::PF == 2) {
                     Regs r0, r1;
@@ -695,6 +691,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 1>>("128x128x32_w2x2_sp4_cil"),
     make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 2, 1>>("128x128x32_w2x2_sp8"),
+    make_entry<Tile<128, 256, 32, 2, 2, 1, 4, 2, 1>>("128x256x32_w2x2_sp4"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 3, 1, 1>>("128x192x32_w2x2_sp8_pf3_il"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 2, 1>>("128x192x32_w2x2_sp8"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1>>("64x64x64_w2x2_sp4"),
@@ -708,6 +705,8 @@ const ConfigEntry kConfigs[] = {
     // specialised with the K range split over KS workgroups
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("32x48x64_k4_sp8_pf3_il_ks2"),
@@ -747,12 +746,12 @@ int config_index(const char *name) {
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     (void)swiglu; (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4");
-    static const int wide = config_index("128x192x32_w2x2_sp8_pf3_il");
+    static const int wide = config_index("128x192x32_w2x2_sp8_pf4_il");
     static const int mid = config_index("64x64x64_w2x2_sp4");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp8_pf3");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il");
     static const int small = config_index("32x48x64_k4_sp4_pf3_cil");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil");
+    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil");
     static const int tiny = config_index("16x48x128_k4_sp4");
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
