@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step: time every workload configuration alone (warm median/min/p90, "
+                         "cold-cache HBM GB/s for the N=768 shapes, torch.matmul fp32 as context) and print "
+                         "a markdown table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (for counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -185,8 +189,141 @@ def cpu_baseline(cases, min_seconds):
     }
 
 
+CONFIGS = [
+    # name, generator, variant keys, M rows used (None: all), cold GB/s reported
+    ("cfg1 matmul", "cfg1", ("X", "W", None), None, True),
+    ("cfg2 matmul_residual", "cfg2", ("X", "W", "R"), None, True),
+    ("cfg2 matmul", "cfg2", ("X", "W", None), None, True),
+    ("cfg3 matmul_residual_swiglu_a", "cfg3", ("G", "U", "W", "R"), None, True),
+    ("cfg4 matmul_w16 lm_head", "cfg4", ("X", "W_lm", None), None, False),
+    ("cfg4b matmul_w16 gate/up", "cfg4", ("X", "W_gu", None), None, False),
+    ("cfg5a matmul_residual_swiglu_a_w16", "cfg5", ("G", "U", "W_down", "R"), None, True),
+    ("cfg5a (M=8191)", "cfg5", ("G", "U", "W_down", "R"), 8191, True),
+    ("cfg5b matmul_w16 lm_head", "cfg5", ("X", "W_lm", None), None, False),
+    ("cfg5b (M=8191)", "cfg5", ("X", "W_lm", None), 8191, False),
+]
+
+
+def time_configs():
+    """Each workload configuration on its own, timed per launch by events
+    that the launch records at the kernel's start and end.  Warm: back-to-
+    back launches (inputs up to cfg 4 stay in the 256 MB Infinity Cache).
+    Cold: a 512 MiB buffer is written between launches, outside the kernel's
+    interval, so its inputs come from HBM.  torch.matmul in fp32 on the
+    same (plain) product is reported as context only."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    sp = st.cuda_stream
+    flush = torch.empty(128 << 20, device=dev)
+    gens = {}
+
+    def d(a, rows=None):
+        a = np.ascontiguousarray(a if rows is None else a[:rows])
+        return torch.from_numpy(a).to(dev)
+
+    rows_out = []
+    for name, gen, keys, rows, cold in CONFIGS:
+        if gen not in gens:
+            gens = {gen: getattr(inputs, gen)()}
+        c = gens[gen]
+        swiglu = len(keys) == 4
+        if swiglu:
+            G, U, W, R = d(c[keys[0]], rows), d(c[keys[1]], rows), d(c[keys[2]]), d(c[keys[3]], rows)
+            M, K = G.shape
+        else:
+            X, W = d(c[keys[0]], rows), d(c[keys[1]])
+            R = d(c[keys[2]], rows) if keys[2] else None
+            M, K = X.shape
+        N = W.shape[1]
+        w16 = W.dtype == torch.float16
+        Y = torch.empty((M, N), device=dev)
+        def launch(ev=(None, None)):
+            if swiglu:
+                return lib.gemm_fwd_swiglu_timed(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(),
+                                                 Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+            return lib.gemm_fwd_timed(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(),
+                                      Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+
+        def sample(n, flush_between):
+            """n launches queued back to back (a flush kernel between them
+            when cold), each timed by its own event pair; read at the end."""
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a, b in evs:
+                a.record(st)
+                b.record(st)
+            torch.cuda.synchronize()
+            for a, b in evs:
+                if flush_between:
+                    flush.fill_(1.0)
+                assert launch((a.cuda_event, b.cuda_event)) == 0
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+        # warm up for a fixed time, not a count, so the clocks have ramped
+        # after the host-side input generation whatever the kernel's length
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            for _ in range(10):
+                assert launch() == 0
+            torch.cuda.synchronize()
+        n = 100 if M * N * K < 1e11 else 30
+        warm = sample(n, False)
+        flops = 2 * M * N * K
+        abytes = M * K * (8 if swiglu else 4) + K * N * (2 if w16 else 4) + M * N * 4 * (2 if R is not None else 1)
+        row = {"config": name, "M": M, "K": K, "N": N, "tile": binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16),
+               "warm_median_us": round(float(np.median(warm)), 2), "warm_min_us": round(float(warm.min()), 2),
+               "warm_p90_us": round(float(np.percentile(warm, 90)), 2),
+               "tflops": round(flops / np.median(warm) / 1e6, 2),
+               "frac_fp32_mfma_peak": round(flops / np.median(warm) / 1e6 / PEAK_FP32_MFMA_TFLOPS, 4)}
+        if cold:
+            cm = float(np.median(sample(n, True)))
+            row["cold_median_us"] = round(cm, 2)
+            row["cold_alg_GBps"] = round(abytes / cm / 1e3, 1)
+        if name.startswith("cfg1"):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(1000):
+                launch()
+            torch.cuda.synchronize()
+            row["amortised_us_per_launch"] = round((time.perf_counter() - t0) / 1000 * 1e6, 2)
+        # context: the plain fp32 product in torch (hipBLASLt); no SwiGLU, no residual
+        A = (torch.nn.functional.silu(G) * U) if swiglu else X
+        Wf = W.float()
+        Yt = torch.empty_like(Y)
+        for _ in range(5):
+            torch.matmul(A, Wf, out=Yt)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            torch.matmul(A, Wf, out=Yt)
+        torch.cuda.synchronize()
+        row["torch_matmul_fp32_us"] = round((time.perf_counter() - t0) / n * 1e6, 2)
+        rows_out.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del Y, Yt, A
+    hdr = ("| config | M×K×N | tile | warm median µs | min | p90 | TFLOP/s | % of 157.3 | cold µs | cold GB/s | "
+           "torch.matmul fp32 µs (plain product) |")
+    print(hdr)
+    print("|" + "---|" * 11)
+    for r in rows_out:
+        print(f"| {r['config']} | {r['M']}×{r['K']}×{r['N']} | {r['tile']} | {r['warm_median_us']} | {r['warm_min_us']} | "
+              f"{r['warm_p90_us']} | {r['tflops']} | {r['frac_fp32_mfma_peak'] * 100:.1f} | {r.get('cold_median_us', '')} | "
+              f"{r.get('cold_alg_GBps', '')} | {r['torch_matmul_fp32_us']} |")
+    c1 = next(r for r in rows_out if r["config"].startswith("cfg1"))
+    print(f"\ncfg1 amortised over 1000 back-to-back launches: {c1['amortised_us_per_launch']} us per launch")
+
+
 def main():
     args = parse()
+    if args.configs:
+        import torch
+        torch.backends.cuda.matmul.allow_tf32 = False
+        time_configs()
+        return
     if args.traffic_from:
         traffic_from(args.traffic_from)
         return
