@@ -153,6 +153,26 @@ __device__ __forceinline__ f32x4 load_f32x4(Rsrc r, int off) {
 
 typedef unsigned int u32x4v __attribute__((vector_size(16)));
 
+// 16-byte buffer load whose destination is LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after `dst` (uniform across the wave), with zeros
+// for an out-of-range offset.  The builtin exists only for the device pass.
+__device__ __forceinline__ void load_f32x4_to_lds(Rsrc r, float *dst, int off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+#else
+    (void)r; (void)dst; (void)off;
+#endif
+}
+
+// s_waitcnt for at most N outstanding vector memory operations (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// maxima, i.e. not waited for).
+template <unsigned N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15u) | (7u << 4) | (15u << 8) | (((N >> 4) & 3u) << 14));
+}
+
 
 // Out-of-range stores (offset >= resource size) are dropped by the hardware.
 __device__ __forceinline__ void store_f32x4(Rsrc r, int off, f32x4 v) {
@@ -182,10 +202,19 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // work overlap on every SIMD (specialised pipeline).  PF: register sets of
 // staged K-stages per staging thread (1 to 5); loads run PF-1 stages ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
-          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2>
+          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2, int FL_ = 0, int NB_ = 2, int DMA_ = 0>
 struct Tile {
     static constexpr bool CIL = CIL_ != 0;  // pipeline fragment reads one k-slice ahead of the MFMAs
     static constexpr int PRIO = PRIO_;      // wave priority of the staging waves
+    // Specialised pipeline only: staging and compute waves hand the NB LDS
+    // stage buffers over through LDS counters instead of one workgroup
+    // barrier per stage, so staging can run up to NB-1 stages ahead.
+    static constexpr bool FL = FL_ != 0;
+    static constexpr int NB = NB_;
+    // Specialised pipeline only: operands that need no arithmetic on the way
+    // (bit 0: plain fp32 A, bit 1: fp32 W) go from memory straight into the
+    // LDS stage by buffer loads with the LDS destination, bypassing VGPRs.
+    static constexpr int DMA = DMA_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WM = WM_, WN = WN_, WK = WK_;
     static constexpr int NP = NP_, PF = PF_, MINB = MINB_;
@@ -200,9 +229,9 @@ struct Tile {
 // and its LDS store.  Each W item is four consecutive columns of one row.
 template <int A_IT, int B_IT, bool SWIGLU, bool W16>
 struct StageRegs {
-    f32x4 a[A_IT];
-    f32x4 u[SWIGLU ? A_IT : 1];
-    typename std::conditional<W16, f16x4, f32x4>::type b[B_IT];
+    f32x4 a[A_IT > 0 ? A_IT : 1];
+    f32x4 u[SWIGLU && A_IT > 0 ? A_IT : 1];
+    typename std::conditional<W16, f16x4, f32x4>::type b[B_IT > 0 ? B_IT : 1];
 };
 
 template <class C, bool SWIGLU, bool W16, bool RESID>
@@ -224,13 +253,21 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int STAGE = BM * BK + BK * BSTR;  // floats per LDS stage
     constexpr int CSTR = BN + 4;            // padded row of the output tile in LDS
     constexpr int CTILE = WK * BM * CSTR;   // floats for the output tile(s) in LDS
-    constexpr int LDS_FLOATS = (2 * STAGE > CTILE) ? 2 * STAGE : CTILE;
+    constexpr int NBUF = C::FL ? C::NB : 2;  // LDS stage buffers
+    static_assert(!C::FL || (SPEC && NBUF >= 2 && NBUF <= 4), "counter hand-over needs staging waves");
+    static_assert(!C::FL || C::DMA == 0, "LDS-destination staging uses the barrier pipeline");
+    static_assert(C::DMA == 0 || C::PF >= 2, "LDS-destination staging needs two register sets");
+    constexpr int LDS_FLOATS = (NBUF * STAGE > CTILE) ? NBUF * STAGE : CTILE;
     constexpr int WBYTES = W16 ? 2 : 4;
     static_assert(BK % 32 == 0, "swizzle needs at least 8 slots per row");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be MFMA tiles");
     static_assert(CH % WK == 0, "K slices must split evenly over waves");
 
     __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    // counter hand-over: ring_cnt[b] counts staging waves that filled buffer
+    // b, ring_cnt[NBUF + b] compute waves that finished reading it (both
+    // only grow during the call)
+    __shared__ unsigned ring_cnt[2 * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -255,8 +292,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
 
     // A (and UP) resources span the tile's valid rows, so rows >= M read as 0.
     const int rows_valid = min(BM, M - m0);
-    const Rsrc rA = make_rsrc(p.A + (size_t)m0 * K, rows_valid * K * 4);
-    const Rsrc rU = SWIGLU ? make_rsrc(p.U + (size_t)m0 * K, rows_valid * K * 4) : rA;
+    // The A (and UP) resources of a stage start at column k0 of the tile's
+    // first row and end with its last valid row, so rows >= M read as 0.
+    const float *Abase = p.A + (size_t)m0 * K;
+    const float *Ubase = SWIGLU ? p.U + (size_t)m0 * K : Abase;
+    const int abytes = rows_valid * K * 4;
     const char *Wbase = static_cast<const char *>(p.W) + (size_t)n0 * WBYTES;
 
     // Per-thread staging coordinates (fixed over the K loop).
@@ -269,36 +309,112 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         a_off[i] = (row * K + slot * 4) * 4;
     }
     // W items: consecutive staging threads take consecutive 4-column groups
-    // of a row, so each load instruction reads contiguous memory.
-    int b_off[B_IT], b_k[B_IT];
+    // of a row, so each load instruction reads contiguous memory.  Rows past
+    // the K range fall outside the stage's W resource, so only items outside
+    // the tile (columns >= N, padding items) need the kOOB offset.
+    int b_off[B_IT];
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
         const int mb = stid + i * NS;
         const int k = mb / NQ, nq = mb % NQ;
         const bool live = (B_IT * NS == B_MB || mb < B_MB) && (n0 + nq * 4 < N);
-        b_k[i] = live ? k : K;  // dead items are always masked
-        b_off[i] = (k * N + nq * 4) * WBYTES;
+        b_off[i] = live ? (k * N + nq * 4) * WBYTES : kOOB;
     }
 
-    typedef StageRegs<A_IT, B_IT, SWIGLU, W16> Regs;
+    // Operands staged by LDS-destination loads, and the register items left.
+    constexpr bool DMA_A = (C::DMA & 1) && !SWIGLU && SPEC;
+    constexpr bool DMA_W = (C::DMA & 2) && !W16 && SPEC;
+    constexpr int A_RIT = DMA_A ? 0 : A_IT;
+    constexpr int B_RIT = DMA_W ? 0 : B_IT;
+    constexpr int REG_LOADS = A_RIT * (SWIGLU ? 2 : 1) + B_RIT;  // register loads per stage
+    typedef StageRegs<A_RIT, B_RIT, SWIGLU, W16> Regs;
+
+    // One LDS-destination load moves 64 float4 slots (1 KiB) into a
+    // contiguous LDS range, lane l into slot l; each lane picks the global
+    // float4 that belongs in its slot, so the swizzled A layout and the
+    // padded W rows come out as the register path writes them (pad slots
+    // and masked elements are fetched out of range and land as zeros).
+    constexpr int W_SPR = NQ + 1;                 // float4 slots per padded W row
+    constexpr int A_CH = A_F4 / 64;               // 64-slot chunks per stage
+    constexpr int W_CH = BK * W_SPR / 64;
+    static_assert(!DMA_A || A_F4 % 64 == 0, "A tile must be whole 64-slot chunks");
+    static_assert(!DMA_W || (BK * W_SPR) % 64 == 0, "padded W tile must be whole 64-slot chunks");
+    constexpr int NPW = SPEC ? C::NP : 1;
+    constexpr int A_DIT = DMA_A ? (A_CH + NPW - 1) / NPW : 0;  // chunks per staging wave
+    constexpr int W_DIT = DMA_W ? (W_CH + NPW - 1) / NPW : 0;
+    const int pw = SPEC ? wave - NC / 64 : 0;     // staging wave index (uniform)
+    int ad_off[A_DIT > 0 ? A_DIT : 1], ad_gk[A_DIT > 0 ? A_DIT : 1];
+#pragma unroll
+    for (int j = 0; j < A_DIT; ++j) {
+        const int q = (pw + j * NPW) * 64 + lane;
+        const int row = q / SL, logical = (q % SL) ^ swz(row);
+        ad_gk[j] = logical * 4;
+        ad_off[j] = (row * K + logical * 4) * 4;
+    }
+    int wd_off[W_DIT > 0 ? W_DIT : 1];
+#pragma unroll
+    for (int j = 0; j < W_DIT; ++j) {
+        const int q = (pw + j * NPW) * 64 + lane;
+        const int k = q / W_SPR, s4 = q % W_SPR;
+        const bool live = s4 < NQ && n0 + s4 * 4 < N;
+        wd_off[j] = live ? (k * N + s4 * 4) * 4 : kOOB;
+    }
+    auto dma_stage = [&](int buf, int k0) {
+        float *S = lds + buf * STAGE;
+        const int krem = kend - k0;
+        if constexpr (DMA_A) {
+            const int arem = abytes - k0 * 4;
+            const Rsrc rA = make_rsrc(Abase + k0, arem > 0 ? arem : 0);
+#pragma unroll
+            for (int j = 0; j < A_DIT; ++j) {
+                const int c = pw + j * NPW;
+                if (A_CH % NPW != 0 && c >= A_CH) break;
+                const int off = ad_gk[j] < krem ? ad_off[j] : kOOB;
+                load_f32x4_to_lds(rA, S + c * 256, off);
+            }
+        }
+        if constexpr (DMA_W) {
+            const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
+                                      krem > 0 ? min(krem, BK) * N * WBYTES : 0);
+#pragma unroll
+            for (int j = 0; j < W_DIT; ++j) {
+                const int c = pw + j * NPW;
+                if (W_CH % NPW != 0 && c >= W_CH) break;
+                load_f32x4_to_lds(rW, S + BM * BK + c * 256, wd_off[j]);
+            }
+        }
+        // keep the register loads that follow behind these in issue order, so
+        // that a vmcnt of the later ones' count covers them
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Wait until at most the register loads of the last n stages are
+    // outstanding, so every LDS-destination load issued before them landed.
+    auto dma_wait = [&](auto n) {
+        if constexpr (DMA_A || DMA_W) wait_vmcnt<decltype(n)::value * REG_LOADS>();
+    };
 
     auto load_stage = [&](Regs &r, int k0) {
+        // per stage only scalar work moves the resources; per item the A
+        // column is checked against the K range (one compare, one select)
+        const int krem = kend - k0;
+        const int arem = abytes - k0 * 4;
+        const Rsrc rA = make_rsrc(Abase + k0, arem > 0 ? arem : 0);
+        const Rsrc rU = SWIGLU ? make_rsrc(Ubase + k0, arem > 0 ? arem : 0) : rA;
 #pragma unroll
-        for (int i = 0; i < A_IT; ++i) {
-            const int off = (a_gk[i] + k0 < kend) ? a_off[i] + k0 * 4 : kOOB;
+        for (int i = 0; i < A_RIT; ++i) {
+            const int off = a_gk[i] < krem ? a_off[i] : kOOB;
             r.a[i] = load_f32x4(rA, off);
             if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, off);
         }
-        // W rows k0 .. k0+BK-1 from a resource based at row k0, so offsets stay
-        // 32-bit whatever K * N is.
-        const int krem = kend - k0;
+        // W rows k0 .. k0+BK-1 from a resource based at row k0 that ends at
+        // the K range, so offsets stay 32-bit whatever K * N is and rows past
+        // the range read as 0.
         const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
                                   krem > 0 ? min(krem, BK) * N * WBYTES : 0);
 #pragma unroll
-        for (int i = 0; i < B_IT; ++i) {
-            const int voff = (b_k[i] < krem) ? b_off[i] : kOOB;
-            if constexpr (W16) r.b[i] = load_f16x4(rW, voff);
-            else r.b[i] = load_f32x4(rW, voff);
+        for (int i = 0; i < B_RIT; ++i) {
+            if constexpr (W16) r.b[i] = load_f16x4(rW, b_off[i]);
+            else r.b[i] = load_f32x4(rW, b_off[i]);
         }
     };
 
@@ -306,7 +422,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         float *As = lds + buf * STAGE;
         float *Bs = As + BM * BK;
 #pragma unroll
-        for (int i = 0; i < A_IT; ++i) {
+        for (int i = 0; i < A_RIT; ++i) {
             const int f = stid + i * NS;
             if (A_IT * NS != A_F4 && f >= A_F4) continue;
             const int row = f / SL, slot = f % SL;
@@ -320,7 +436,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
         }
 #pragma unroll
-        for (int i = 0; i < B_IT; ++i) {
+        for (int i = 0; i < B_RIT; ++i) {
             const int mb = stid + i * NS;
             if (B_IT * NS != B_MB && mb >= B_MB) continue;
             const int k = mb / NQ, nq = mb % NQ;
@@ -421,7 +537,71 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     //  PF == 1: the loads of stage s+1 overlap the MFMAs of stage s.
     const int nstages = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-    if constexpr (SPEC) {
+    // Bounded wait for a ring counter: a wave polls the count (one LDS read
+    // per try, then a short sleep) until it reaches target.  The bound only
+    // keeps a wave from spinning forever should the hand-over ever break;
+    // it is far beyond any stage's duration.
+    auto ring_wait = [&](const unsigned *cnt, unsigned target) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            const unsigned v = __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
+    // The wave's LDS accesses complete (release) before its count moves.
+    auto ring_signal = [&](unsigned *cnt) {
+        if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    constexpr unsigned NCW = WM * WN * WK;  // compute waves
+    constexpr unsigned NSW = C::NP;          // staging waves
+
+    if constexpr (C::FL) {
+        if (tid < 2 * NBUF) ring_cnt[tid] = 0u;
+        __syncthreads();
+        if (stages) {
+            __builtin_amdgcn_s_setprio(C::PRIO);
+            if (nstages > 0) {
+                // PF register sets, stage t in set t % PF; a step waits until
+                // buffer t % NBUF has been read for stage t - NBUF, stores
+                // stage t, counts it, and issues the loads of stage t + PF.
+                constexpr int PF = C::PF;
+                Regs r[PF];
+#pragma unroll
+                for (int j = 0; j < PF; ++j) load_stage(r[j], kbeg + j * BK);
+                auto step = [&](Regs &rr, int t) {
+                    const int b = t % NBUF;
+                    if (t >= NBUF) ring_wait(&ring_cnt[NBUF + b], NCW * (unsigned)(t / NBUF));
+                    store_stage(rr, b);
+                    ring_signal(&ring_cnt[b]);
+                };
+                int s = 0;
+                for (; s + PF <= nstages; s += PF) {
+#pragma unroll
+                    for (int j = 0; j < PF; ++j) {
+                        step(r[j], s + j);
+                        load_stage(r[j], kbeg + (s + j + PF) * BK);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j + 1 < PF; ++j)
+                    if (s + j < nstages) step(r[j], s + j);
+            }
+            __syncthreads();  // every buffer read: the output tile may reuse LDS
+            __syncthreads();  // the epilogue's barrier
+            if constexpr (KS > 1) {
+                __syncthreads();  // partials stored
+                __syncthreads();  // arrival counted
+            }
+            return;
+        }
+        for (int t = 0; t < nstages; ++t) {
+            const int b = t % NBUF;
+            ring_wait(&ring_cnt[b], NSW * (unsigned)(t / NBUF + 1));
+            compute_stage(b);
+            ring_signal(&ring_cnt[NBUF + b]);
+        }
+        __syncthreads();  // every buffer read: the output tile may reuse LDS
+    } else if constexpr (SPEC) {
         // Staging waves run their own loop, one stage ahead of the compute
         // waves, and meet them at the same barriers (equal counts on both
         // sides, including the K-split reduction's).  Keeping the two loops
@@ -433,32 +613,41 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             // holding the next barrier back.
             __builtin_amdgcn_s_setprio(C::PRIO);
             if (nstages > 0) {
-                if constexpr (C::PF >= 3) {
+                if constexpr (C::PF >= 3 || DMA_A || DMA_W) {
                     // PF register sets, stage t in set t % PF: each step
                     // first issues the loads of stage s+PF into the set just
                     // stored, then combines and stores stage s+1, so the
                     // address unit drains while the VALU works and every
-                    // load has PF-1 steps to land.
+                    // load has PF-1 steps to land.  LDS-destination loads of
+                    // stage s+1 go out first in the step (their buffer is
+                    // free since the last barrier) and are waited for just
+                    // before the barrier.
                     constexpr int PF = C::PF;
                     Regs r[PF];
+                    dma_stage(0, kbeg);
 #pragma unroll
                     for (int j = 0; j < PF; ++j) load_stage(r[j], kbeg + j * BK);
                     store_stage(r[0], 0);
+                    dma_wait(std::integral_constant<unsigned, PF - 1>{});
                     __syncthreads();
                     int s = 0;
                     for (; s + PF <= nstages; s += PF) {
 #pragma unroll
                         for (int j = 0; j < PF; ++j) {
+                            dma_stage((s + j + 1) & 1, kbeg + (s + j + 1) * BK);
                             load_stage(r[j], kbeg + (s + j + PF) * BK);
                             store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
                             interleave_hint();
+                            dma_wait(std::integral_constant<unsigned, 1>{});
                             __syncthreads();
                         }
                     }
 #pragma unroll
                     for (int j = 0; j + 1 < PF; ++j) {
                         if (s + j < nstages) {
+                            dma_stage((s + j + 1) & 1, kbeg + (s + j + 1) * BK);
                             store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
+                            dma_wait(std::integral_constant<unsigned, 0>{});
                             __syncthreads();
                         }
                     }
@@ -706,6 +895,19 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 0, 2, 1, 2, 0, 2, 2>>("32x96x64_w1x2_k2_sp8_pf4_ks2_cil_dW"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 0, 2, 1, 2, 0, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 0, 2, 1>>("128x128x32_w2x2_sp4_dA"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 0, 1, 0, 2, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_dA"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("64x48x64_w2x1_k2_sp4_pf2_dAW"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 0, 1, 0, 2, 0, 2, 2>>("16x96x64_k4_sp8_pf3_dW"),
+    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 0, 4, 1, 2, 0, 2, 2>>("32x192x64_w1x4_sp8_pf3_ks4_cil_dW"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 0, 4, 1, 2, 0, 2, 2>>("64x96x64_w2x2_sp8_pf3_ks4_cil_dW"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 0, 1, 0, 2, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_dA"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1, 2, 0, 2, 2>>("32x48x64_k4_sp4_pf3_cil_dW"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
@@ -745,14 +947,14 @@ int config_index(const char *name) {
 // with the K range split over waves for small grids.
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     (void)swiglu; (void)w16;
-    static const int big = config_index("128x128x32_w2x2_sp4");
+    static const int big = config_index("128x128x32_w2x2_sp4_pf3_dA");
     static const int wide = config_index("128x192x32_w2x2_sp8_pf4_il");
     static const int mid = config_index("64x64x64_w2x2_sp4");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il");
-    static const int small = config_index("32x48x64_k4_sp4_pf3_cil");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf2_dAW");
+    static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil");
-    static const int tiny = config_index("16x48x128_k4_sp4");
+    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW");
+    static const int tiny = config_index("16x48x128_k4_sp4_dAW");
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
     static const bool complete = big >= 0 && wide >= 0 && mid >= 0 && narrow >= 0 && small >= 0 &&
