@@ -202,15 +202,10 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // work overlap on every SIMD (specialised pipeline).  PF: register sets of
 // staged K-stages per staging thread (1 to 5); loads run PF-1 stages ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
-          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2, int FL_ = 0, int NB_ = 2, int DMA_ = 0>
+          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2, int DMA_ = 0>
 struct Tile {
     static constexpr bool CIL = CIL_ != 0;  // pipeline fragment reads one k-slice ahead of the MFMAs
     static constexpr int PRIO = PRIO_;      // wave priority of the staging waves
-    // Specialised pipeline only: staging and compute waves hand the NB LDS
-    // stage buffers over through LDS counters instead of one workgroup
-    // barrier per stage, so staging can run up to NB-1 stages ahead.
-    static constexpr bool FL = FL_ != 0;
-    static constexpr int NB = NB_;
     // Specialised pipeline only: operands that need no arithmetic on the way
     // (bit 0: plain fp32 A, bit 1: fp32 W) go from memory straight into the
     // LDS stage by buffer loads with the LDS destination, bypassing VGPRs.
@@ -253,21 +248,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int STAGE = BM * BK + BK * BSTR;  // floats per LDS stage
     constexpr int CSTR = BN + 4;            // padded row of the output tile in LDS
     constexpr int CTILE = WK * BM * CSTR;   // floats for the output tile(s) in LDS
-    constexpr int NBUF = C::FL ? C::NB : 2;  // LDS stage buffers
-    static_assert(!C::FL || (SPEC && NBUF >= 2 && NBUF <= 4), "counter hand-over needs staging waves");
-    static_assert(!C::FL || C::DMA == 0, "LDS-destination staging uses the barrier pipeline");
     static_assert(C::DMA == 0 || C::PF >= 2, "LDS-destination staging needs two register sets");
-    constexpr int LDS_FLOATS = (NBUF * STAGE > CTILE) ? NBUF * STAGE : CTILE;
+    constexpr int LDS_FLOATS = (2 * STAGE > CTILE) ? 2 * STAGE : CTILE;
     constexpr int WBYTES = W16 ? 2 : 4;
     static_assert(BK % 32 == 0, "swizzle needs at least 8 slots per row");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be MFMA tiles");
     static_assert(CH % WK == 0, "K slices must split evenly over waves");
 
     __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
-    // counter hand-over: ring_cnt[b] counts staging waves that filled buffer
-    // b, ring_cnt[NBUF + b] compute waves that finished reading it (both
-    // only grow during the call)
-    __shared__ unsigned ring_cnt[2 * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -537,71 +525,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     //  PF == 1: the loads of stage s+1 overlap the MFMAs of stage s.
     const int nstages = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-    // Bounded wait for a ring counter: a wave polls the count (one LDS read
-    // per try, then a short sleep) until it reaches target.  The bound only
-    // keeps a wave from spinning forever should the hand-over ever break;
-    // it is far beyond any stage's duration.
-    auto ring_wait = [&](const unsigned *cnt, unsigned target) {
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-            const unsigned v = __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (__builtin_amdgcn_readfirstlane(v) >= target) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-    };
-    // The wave's LDS accesses complete (release) before its count moves.
-    auto ring_signal = [&](unsigned *cnt) {
-        if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    };
-    constexpr unsigned NCW = WM * WN * WK;  // compute waves
-    constexpr unsigned NSW = C::NP;          // staging waves
-
-    if constexpr (C::FL) {
-        if (tid < 2 * NBUF) ring_cnt[tid] = 0u;
-        __syncthreads();
-        if (stages) {
-            __builtin_amdgcn_s_setprio(C::PRIO);
-            if (nstages > 0) {
-                // PF register sets, stage t in set t % PF; a step waits until
-                // buffer t % NBUF has been read for stage t - NBUF, stores
-                // stage t, counts it, and issues the loads of stage t + PF.
-                constexpr int PF = C::PF;
-                Regs r[PF];
-#pragma unroll
-                for (int j = 0; j < PF; ++j) load_stage(r[j], kbeg + j * BK);
-                auto step = [&](Regs &rr, int t) {
-                    const int b = t % NBUF;
-                    if (t >= NBUF) ring_wait(&ring_cnt[NBUF + b], NCW * (unsigned)(t / NBUF));
-                    store_stage(rr, b);
-                    ring_signal(&ring_cnt[b]);
-                };
-                int s = 0;
-                for (; s + PF <= nstages; s += PF) {
-#pragma unroll
-                    for (int j = 0; j < PF; ++j) {
-                        step(r[j], s + j);
-                        load_stage(r[j], kbeg + (s + j + PF) * BK);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j + 1 < PF; ++j)
-                    if (s + j < nstages) step(r[j], s + j);
-            }
-            __syncthreads();  // every buffer read: the output tile may reuse LDS
-            __syncthreads();  // the epilogue's barrier
-            if constexpr (KS > 1) {
-                __syncthreads();  // partials stored
-                __syncthreads();  // arrival counted
-            }
-            return;
-        }
-        for (int t = 0; t < nstages; ++t) {
-            const int b = t % NBUF;
-            ring_wait(&ring_cnt[b], NSW * (unsigned)(t / NBUF + 1));
-            compute_stage(b);
-            ring_signal(&ring_cnt[NBUF + b]);
-        }
-        __syncthreads();  // every buffer read: the output tile may reuse LDS
-    } else if constexpr (SPEC) {
+    if constexpr (SPEC) {
         // Staging waves run their own loop, one stage ahead of the compute
         // waves, and meet them at the same barriers (equal counts on both
         // sides, including the K-split reduction's).  Keeping the two loops
@@ -895,19 +819,19 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 0, 2, 1, 2, 0, 2, 2>>("32x96x64_w1x2_k2_sp8_pf4_ks2_cil_dW"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 0, 2, 1, 2, 0, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 0, 2, 1>>("128x128x32_w2x2_sp4_dA"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 0, 1, 0, 2, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_dA"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("64x48x64_w2x1_k2_sp4_pf2_dAW"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 0, 1, 0, 2, 0, 2, 2>>("16x96x64_k4_sp8_pf3_dW"),
-    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 0, 4, 1, 2, 0, 2, 2>>("32x192x64_w1x4_sp8_pf3_ks4_cil_dW"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 0, 4, 1, 2, 0, 2, 2>>("64x96x64_w2x2_sp8_pf3_ks4_cil_dW"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 0, 1, 0, 2, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_dA"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1, 2, 0, 2, 2>>("32x48x64_k4_sp4_pf3_cil_dW"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
-    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf4_ks2_cil_dW"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_dA"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 0, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_dA"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1, 0, 1, 0, 2, 3>>("64x48x64_w2x1_k2_sp4_pf2_dAW"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 0, 1, 0, 2, 2>>("16x96x64_k4_sp8_pf3_dW"),
+    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 0, 4, 1, 2, 2>>("32x192x64_w1x4_sp8_pf3_ks4_cil_dW"),
+    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 0, 4, 1, 2, 2>>("64x96x64_w2x2_sp8_pf3_ks4_cil_dW"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 0, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_dA"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1, 2, 2>>("32x48x64_k4_sp4_pf3_cil_dW"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
