@@ -821,6 +821,9 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf4_ks2_cil_dW"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_dA"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 0, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_dA"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1, 0, 1, 0, 2, 3>>("64x48x64_w2x1_k2_sp4_pf2_dAW"),
@@ -871,13 +874,13 @@ int config_index(const char *name) {
 // with the K range split over waves for small grids.
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     (void)swiglu; (void)w16;
-    static const int big = config_index("128x128x32_w2x2_sp4_pf3_dA");
+    static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
     static const int wide = config_index("128x192x32_w2x2_sp8_pf4_il");
     static const int mid = config_index("64x64x64_w2x2_sp4");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf2_dAW");
+    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il_dA");
     static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW");
+    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int tiny = config_index("16x48x128_k4_sp4_dAW");
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
