@@ -11,9 +11,12 @@
  *   matmul_residual_swiglu_a      Y = (silu(GATE) * UP) @ W + R
  *   *_w16                         the same with IEEE binary16 weights
  *
- * with silu(x) = x * sigmoid(x) and the sign-branched sigmoid of the page
+ * with silu(x) = x * sigmoid(x) and the sigmoid of the page
  * "ffn_gelu_backward ve ffn_swiglu_backward — FFN Activation Backward"
  * (https://llm.istanbul/learn/tr/09_backward_ffn), section "Türevler / SiLU'".
+ * The page branches on the sign of x; the kernels evaluate the same function
+ * unbranched, as g * u / (1 + exp(-g)), whose overflow for g < -88.7 gives
+ * the correct limit, zero.
  * The SwiGLU combine is applied while the A operand is staged, so the hidden
  * [M x K] matrix is never written ("Önemli Optimizasyonlar" §3 of the first
  * page).
