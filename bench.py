@@ -64,6 +64,12 @@ def parse():
                          "a markdown table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (for counter calibration)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the step: run the MFMA ceiling probe (independent fp32 MFMAs only) at 4, 8 "
+                         "and 16 waves per CU and print the sustained TFLOP/s and engine clock")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="turn the rocprofv3 counter runs under DIR (p1/, p2/) into "
+                         + os.path.relpath(os.path.join(ROOT, "profiles", "seq512_counters.md"), ROOT) + " and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="turn the rocprofv3 counter runs under DIR (fetch/, write/, copy_fetch/, copy_write/) "
                          "into " + os.path.relpath(TRAFFIC_FILE, ROOT) + " and exit")
@@ -93,6 +99,127 @@ def _counter_rows(run_dir):
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
     with open(files[0]) as f:
         return list(csv.DictReader(f))
+
+
+def mfma_ceiling():
+    """What the fp32 matrix cores sustain with nothing but independent MFMAs
+    in flight: the ceiling that the roofline's published peak stands for."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "tiled_dense_gemm_matmul_amd", "libmfmaprobe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.mfma_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mfma_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mfma_probe_flops.restype = ctypes.c_longlong
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    iters, reps = 8192, 10
+    out = []
+    for waves_per_cu in (4, 8, 16):
+        blocks = 256 * waves_per_cu // 4
+        sink = torch.empty(blocks * 256, device=dev)
+        clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+
+        def launch():
+            rc = lib.mfma_probe_launch(sink.data_ptr(), clocks.data_ptr(), blocks, iters, st.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"mfma_probe_launch returned {rc}")
+
+        # clocks ramp after host-side work: warm up for at least 0.3 s
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            launch()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            launch()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        c = clocks.view(blocks, 2).cpu().double()
+        mhz = float(c[:, 0].sum() / c[:, 1].sum() * 100.0)
+        tflops = lib.mfma_probe_flops(blocks, iters) / (ms * 1e-3) / 1e12
+        out.append({"waves_per_cu": waves_per_cu, "ms": round(ms, 4), "tflops": round(tflops, 1),
+                    "frac_of_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4), "clock_mhz": round(mhz)})
+        print(json.dumps(out[-1]), flush=True)
+    return out
+
+
+COUNTER_PASSES = {
+    "p1": "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+          "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_MFMA SQ_INSTS_VALU GRBM_GUI_ACTIVE",
+    "p2": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_VALU_MFMA_COEXEC_CYCLES "
+          "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+}
+STEP_LABELS = ["qkvo_residual", "qkvo", "ffn_down", "ffn_gate_up", "lm_head"]   # launch order in a step
+
+
+def counters_from(base):
+    """Per-kernel hardware counters of the step (two rocprofv3 --pmc runs of
+    this script) as a markdown table in profiles/seq512_counters.md."""
+    import collections
+    import statistics
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
+    for run in COUNTER_PASSES:
+        rows = [r for r in _counter_rows(os.path.join(base, run)) if "gemm_fwd_kernel" in r["Kernel_Name"]]
+        order = {d: i for i, d in enumerate(sorted({int(r["Dispatch_Id"]) for r in rows}))}
+        for r in rows:
+            k = STEP_LABELS[order[int(r["Dispatch_Id"])] % STEP_KERNELS]
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    shapes = {name: shape_of(case) for name, case in workload()}
+    simds = 1024
+    lm_clock = statistics.mean(vals["lm_head"]["GRBM_GUI_ACTIVE"]) / 8 / statistics.median(durs["lm_head"])
+    lines = [
+        "# Hardware counters of the seq-512 forward step (bench.py)",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host), one counter set per run:",
+        "",
+    ]
+    for run, ctrs in COUNTER_PASSES.items():
+        lines.append(f"    rocprofv3 --pmc {ctrs} -f csv -d $R/gpurun_out/counters/{run} -o pmc -- "
+                     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu")
+    lines += [
+        "    python3 bench.py --counters-from gpurun_out/counters      # writes this file",
+        "",
+        "Averages over every launch of each kernel in those runs.  Counter collection serialises launches and",
+        "slows the kernels (the `µs under counters` column), so the busy fractions are lower than in an",
+        "unprofiled run; the instruction counts are exact.",
+        "",
+        "- MFMA count / ideal = SQ_INSTS_MFMA / (2MNK / 2048), the flops of one v_mfma_f32_16x16x4_f32.",
+        "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (32 per MFMA, summed over SIMDs) / (1024 SIMDs x 2400 MHz x duration).",
+        "  The lm_head runs long enough for GRBM_GUI_ACTIVE / 8 XCDs / duration to give the clock: "
+        + f"{lm_clock:.0f} MHz.",
+        "- other VALU per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (the VALU count includes the MFMAs);",
+        "  co-issue = SQ_VALU_MFMA_COEXEC_CYCLES, cycles in which a VALU instruction issued while the MFMA unit was busy.",
+        "- LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).",
+        "",
+        "| kernel | M×K×N | launches | µs under counters | MFMA count / ideal | MFMA busy | "
+        "other VALU per MFMA | co-issue cycles | LDS instr per MFMA | LDS conflict | L2 hit |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k in STEP_LABELS:
+        v = {c: statistics.mean(x) for c, x in vals[k].items()}
+        d = statistics.median(durs[k])
+        M, K, N = shapes[k]
+        ideal = 2 * M * K * N / 2048
+        lines.append(
+            f"| {k} | {M}×{K}×{N} | {len(vals[k]['SQ_INSTS_MFMA'])} | {d:.1f} | "
+            f"{v['SQ_INSTS_MFMA'] / ideal:.3f} | {100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * 2400 * d):.1f}% | "
+            f"{(v['SQ_INSTS_VALU'] - v['SQ_INSTS_MFMA']) / v['SQ_INSTS_MFMA']:.2f} | "
+            f"{v['SQ_VALU_MFMA_COEXEC_CYCLES']:.0f} | "
+            f"{v['SQ_INSTS_LDS'] / v['SQ_INSTS_MFMA']:.3f} | "
+            f"{100 * v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.1f}% | "
+            f"{100 * v['TCC_HIT_sum'] / (v['TCC_HIT_sum'] + v['TCC_MISS_sum']):.1f}% |")
+    out = os.path.join(ROOT, "profiles", "seq512_counters.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def traffic_from(base):
@@ -162,6 +289,17 @@ def shape_of(case):
     return A.shape[0], A.shape[1], case["W"].shape[1]
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cases, min_seconds):
     """The fp64 oracle on whole steps (every output row of the five
     products), repeated until at least min_seconds have passed."""
@@ -183,6 +321,7 @@ def cpu_baseline(cases, min_seconds):
         "value": reps * step_flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{reps} whole steps (all rows of the 5 products, "
                   f"{reps * step_flops / 1e9:.1f} GFLOP of fp64) in {dt:.1f} s",
@@ -323,6 +462,12 @@ def main():
         import torch
         torch.backends.cuda.matmul.allow_tf32 = False
         time_configs()
+        return
+    if args.counters_from:
+        counters_from(args.counters_from)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     if args.traffic_from:
         traffic_from(args.traffic_from)

@@ -40,6 +40,27 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), f"libgemmfwd.so does not export {n}"
 
 
+def test_probe_library_exports_its_header():
+    """The MFMA ceiling probe (measurement support for bench.py) exports what
+    include/mfma_probe.h declares and rejects bad arguments without a launch."""
+    path = os.path.join(ROOT, "tiled_dense_gemm_matmul_amd", "libmfmaprobe.so")
+    if not os.path.exists(path):
+        pytest.skip("libmfmaprobe.so not built")
+    with open(os.path.join(ROOT, "include", "mfma_probe.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mfma_probe_[a-z_]+)\s*\(", text)))
+    assert names == ["mfma_probe_flops", "mfma_probe_launch"]
+    probe = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(probe, n)
+    probe.mfma_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.mfma_probe_flops.restype = ctypes.c_longlong
+    assert probe.mfma_probe_launch(None, None, 1, 1, None) == -1
+    assert probe.mfma_probe_launch(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 0, 1, None) == -1
+    assert probe.mfma_probe_launch(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 1, 0, None) == -1
+    assert probe.mfma_probe_flops(256, 8192) == 256 * 4 * 8192 * 8 * 2048
+
+
 def test_status_codes_match_header(lib):
     for name in ["GEMM_OK", "GEMM_ERR_NULL", "GEMM_ERR_SHAPE", "GEMM_ERR_ALIGN", "GEMM_ERR_DTYPE",
                  "GEMM_ERR_ALIAS", "GEMM_ERR_LAUNCH", "GEMM_ERR_CONFIG"]:

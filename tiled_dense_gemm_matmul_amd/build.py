@@ -13,6 +13,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gemm_fwd.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemmfwd.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "mfma_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmfmaprobe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
@@ -20,16 +22,27 @@ HIPCC_FLAGS = [
 ]
 
 
-def build_library(verbose: bool = False) -> str:
+def _hipcc(src: str, lib: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_library(verbose: bool = False) -> str:
+    """The GEMM library (every kernel of the forward family)."""
+    return _hipcc(SRC, LIB, verbose)
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The MFMA ceiling probe used by bench.py --mfma-ceiling."""
+    return _hipcc(PROBE_SRC, PROBE_LIB, verbose)
 
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_probe(verbose=True))
