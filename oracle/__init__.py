@@ -17,6 +17,12 @@ Definition followed (pages of the llm.istanbul/learn series):
 * "ffn_gelu_backward ve ffn_swiglu_backward — FFN Activation Backward",
   section "Türevler / SiLU'": silu(x) = x * sigmoid(x) with the sign-branched
   sigmoid.
+* The backward linear family that "Ne Yapar?" names (matmul_t, matmul_at,
+  their _acc forms and matmul_at_swiglu_a), read from the names:
+  dX = dY @ W^T, dW = A^T @ dY with A = X or silu(GATE) * UP, and "_acc"
+  adds the product to the output's previous value.  ``matmul_t`` and
+  ``matmul_at`` are those definitions written out: an explicit transpose
+  (a copy) followed by the pinned contraction ``gemm`` / ``gemm_f64a``.
 
 Every exported function is pinned by ``tests/test_oracle.py``.
 """
@@ -251,3 +257,41 @@ def compare(y, y_ref, scale, tol):
         "worst": tuple(int(v) for v in worst),
         "n": int(ratio.size),
     }
+
+
+def matmul_t(dY, W, Y0=None, rows=None, want_scale=False, threads=0):
+    """matmul_t (Y0 None) or matmul_t_acc: dX = dY @ W^T (+ Y0).
+
+    dY [M, N] float32, W [K, N] float32 (the forward's weight), Y0 [M, K]
+    float32 or None.  Returns dX [len(rows), K] float64 (and the scale
+    sum_n |dy_mn||w_kn| if want_scale), as gemm() does.
+    """
+    W = _f32(W, "W")
+    Wt = np.ascontiguousarray(W.T)          # [N, K]: the transposed weight
+    return gemm(dY, Wt, R=Y0, rows=rows, want_scale=want_scale, threads=threads)
+
+
+def matmul_at(X, dY, Y0=None, U=None, rows=None, want_scale=False, threads=0):
+    """matmul_at / matmul_at_acc / matmul_at_swiglu_a / matmul_at_acc_swiglu_a:
+    dW = A^T @ dY (+ Y0), A = X, or silu(X) * U when U is given (X = GATE).
+
+    X (and U) [M, K] float32, dY [M, N] float32, Y0 [K, N] float32 or None.
+    rows: None or output rows (indices into K).  Returns dW [len(rows), N]
+    float64 (and the scale sum_m |a_mk||dy_mn| if want_scale).
+    """
+    X = _f32(X, "X")
+    dY = _f32(dY, "dY")
+    Y0 = _f32(Y0, "Y0")
+    if U is None:
+        At = np.ascontiguousarray(X.T)      # [K, M]
+        return gemm(At, dY, R=Y0, rows=rows, want_scale=want_scale, threads=threads)
+    H = a_operand(X, U)                     # [M, K] float64, the combine in double
+    Ht = np.ascontiguousarray(H.T)
+    idx = np.arange(Ht.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    Ht = np.ascontiguousarray(Ht[idx])
+    R = None if Y0 is None else np.ascontiguousarray(Y0[idx])
+    y = gemm_f64a(Ht, dY, R=R, threads=threads)
+    if not want_scale:
+        return y
+    b = gemm_f64a(np.abs(Ht), np.ascontiguousarray(np.abs(dY)), threads=threads)
+    return y, b
