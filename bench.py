@@ -64,6 +64,9 @@ def parse():
                          "a markdown table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (for counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the step: time the backward products (matmul_t, matmul_at, _acc, "
+                         "_swiglu_a) at the seq-512 model's shapes and print a markdown table")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the step: run the MFMA ceiling probe (independent fp32 MFMAs only) at 4, 8 "
                          "and 16 waves per CU and print the sustained TFLOP/s and engine clock")
@@ -99,6 +102,81 @@ def _counter_rows(run_dir):
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
     with open(files[0]) as f:
         return list(csv.DictReader(f))
+
+
+BACKWARD = [
+    # label, op, M, K, N (forward names: M tokens, K inputs, N outputs)
+    ("qkvo dX", "matmul_t", 512, 768, 768),
+    ("ffn_down dH", "matmul_t", 512, 3072, 768),
+    ("ffn_gate_up dX", "matmul_t_acc", 512, 768, 3072),
+    ("lm_head dX", "matmul_t", 512, 768, 16384),
+    ("qkvo dW", "matmul_at", 512, 768, 768),
+    ("ffn_gate_up dW", "matmul_at_acc", 512, 768, 3072),
+    ("ffn_down dW (SwiGLU recomputed)", "matmul_at_swiglu_a", 512, 3072, 768),
+    ("lm_head dW", "matmul_at", 512, 768, 16384),
+]
+
+
+def time_backward():
+    """The backward products at the seq-512 model's shapes, each on its own:
+    batches of back-to-back launches between two events (so the figure
+    includes the launch gaps), after at least 0.2 s of warm-up; torch.matmul
+    in fp32 on the same plain product as context."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    rows = []
+    lines = ["| product | kernel | M×K×N (forward names) | output | µs per launch | TFLOP/s | % of 157.3 | "
+             "torch.matmul fp32 µs |", "|---|---|---|---|---|---|---|---|"]
+    for label, op, M, K, N in BACKWARD:
+        c = inputs.backward_case(M + K + N, M, K, N, swiglu="swiglu" in op, acc="acc" in op)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in c.items()}
+        acc = "acc" in op
+        if op.startswith("matmul_t"):
+            out = t["dX0"].clone() if acc else torch.empty((M, K), device=dev)
+            run = lambda: binding.matmul_t(t["dY"], t["W"], out=out, acc=acc)
+            ref = lambda: torch.matmul(t["dY"], t["W"].t())
+            kcfg = binding.kernel_config(M, N, K)
+        else:
+            out = t["dW0"].clone() if acc else torch.empty((K, N), device=dev)
+            if "swiglu" in op:
+                run = lambda: binding.matmul_at_swiglu_a(t["G"], t["U"], t["dY"], out=out, acc=acc)
+                ref = lambda: torch.matmul((torch.nn.functional.silu(t["G"]) * t["U"]).t(), t["dY"])
+            else:
+                run = lambda: binding.matmul_at(t["X"], t["dY"], out=out, acc=acc)
+                ref = lambda: torch.matmul(t["X"].t(), t["dY"])
+            kcfg = binding.kernel_config(K, M, N, swiglu="swiglu" in op)
+
+        def batch(fn, n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(n):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            batch(run, 10)
+        us = float(np.median([batch(run, 50) for _ in range(5)]))
+        for _ in range(3):
+            ref()
+        tus = float(np.median([batch(ref, 20) for _ in range(3)]))
+        flops = 2 * M * K * N
+        tf = flops / us / 1e6
+        shape_out = f"{M}×{K}" if op.startswith("matmul_t") else f"{K}×{N}"
+        row = {"product": label, "op": op, "M": M, "K": K, "N": N, "tile": kcfg, "us": round(us, 2),
+               "tflops": round(tf, 2), "frac_fp32_mfma_peak": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+               "torch_matmul_fp32_us": round(tus, 2)}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        lines.append(f"| {label} | {op} [{kcfg}] | {M}×{K}×{N} | {shape_out} | {us:.2f} | {tf:.1f} | "
+                     f"{100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f} | {tus:.2f} |")
+    print("\n".join(lines))
+    return rows
 
 
 def mfma_ceiling():
@@ -468,6 +546,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.backward:
+        time_backward()
         return
     if args.traffic_from:
         traffic_from(args.traffic_from)

@@ -134,6 +134,57 @@ int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, con
                           int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream,
                           void *start, void *stop);
 
+/* Backward-product flags. */
+#define GEMM_FLAG_ACC 0x2u /* add the product to the output's current contents (the *_acc kernels) */
+
+/*
+ * Backward linear family.  The page "matmul ve matmul_residual — Tiled
+ * Matrix Multiply (Forward)" names these kernels in section "Ne Yapar?"
+ * (matmul_t, matmul_t_acc, matmul_at, matmul_at_acc, matmul_at_swiglu_a,
+ * matmul_at_acc_swiglu_a) and defers them to a page that is not available;
+ * "ffn_gelu_backward ve ffn_swiglu_backward" (section on the pipeline step)
+ * says that they do the GEMM part of the backward FFN.  The operations are
+ * read from the names: "t" multiplies by the transposed weight (the input
+ * gradient of a linear layer), "at" by the transposed activation (its weight
+ * gradient), "_acc" accumulates into the output, "_swiglu_a" recomputes the
+ * activation A = silu(GATE) * UP while it is staged, as the forward does.
+ * Shapes use the forward's names: M rows (tokens), K inputs, N outputs.
+ *
+ *   gemm_matmul_t:            dX [M x K]  = dY [M x N] @ W^T,  W the forward's [K x N] weight
+ *   gemm_matmul_at:           dW [K x N]  = X^T @ dY,          X [M x K]
+ *   gemm_matmul_at_swiglu_a:  dW [K x N]  = (silu(GATE) * UP)^T @ dY,  GATE, UP [M x K]
+ *
+ * With GEMM_FLAG_ACC the product is added to the output (out = out + product,
+ * the output read before it is written); otherwise the output is overwritten.
+ * All arrays are fp32, dense and row-major, 16-byte aligned, device pointers
+ * owned by the caller; the output overlaps no input.  K % 4 == 0 and
+ * N % 4 == 0; M (the contraction of matmul_at) is unrestricted; limits as
+ * for gemm_fwd.  An empty output enqueues nothing; an empty contraction
+ * writes zeros (or leaves the output unchanged with GEMM_FLAG_ACC).  Flags
+ * other than GEMM_FLAG_ACC give GEMM_ERR_DTYPE.  The split-K workspace rules
+ * of gemm_fwd apply.  Returns GEMM_OK or a negative status, validated before
+ * anything is enqueued.
+ */
+int gemm_matmul_t(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                  void *stream);
+int gemm_matmul_at(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                   void *stream);
+int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M, int64_t K,
+                            int64_t N, uint32_t flags, void *stream);
+
+/* The same with an explicit configuration of the backward table (config >= 0,
+ * below gemm_bwd_num_configs()), or the library's choice (config < 0). */
+int gemm_matmul_t_cfg(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                      int config, void *stream);
+int gemm_matmul_at_cfg(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                       int config, void *stream);
+int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
+                                int64_t K, int64_t N, uint32_t flags, int config, void *stream);
+
+/* Number and static names of the backward products' configurations. */
+int gemm_bwd_num_configs(void);
+const char *gemm_bwd_config_name(int config);
+
 /* Number of tile configurations compiled into the library. */
 int gemm_num_configs(void);
 

@@ -167,3 +167,27 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         binding.matmul(x, x)
+
+
+def test_backward_validation(lib):
+    """matmul_t / matmul_at / matmul_at_swiglu_a reject bad arguments
+    synchronously (fake host pointers; nothing reaches a device)."""
+    NULL, SHAPE, ALIGN = _status("GEMM_ERR_NULL"), _status("GEMM_ERR_SHAPE"), _status("GEMM_ERR_ALIGN")
+    DTYPE, ALIAS, CONFIG = _status("GEMM_ERR_DTYPE"), _status("GEMM_ERR_ALIAS"), _status("GEMM_ERR_CONFIG")
+    ACC = 0x2
+    t = lambda dy=X, w=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_t_cfg(dy, w, y, M, K, N, f, c, None)
+    at = lambda x=X, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_cfg(x, dy, y, M, K, N, f, c, None)
+    ats = lambda g=X, u=U, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_swiglu_a_cfg(
+        g, u, dy, y, M, K, N, f, c, None)
+    assert t(dy=None) == NULL and t(w=None) == NULL and t(y=None) == NULL
+    assert at(x=None) == NULL and at(dy=None) == NULL and ats(u=None) == NULL
+    assert t(K=6) == SHAPE and t(N=6) == SHAPE and at(K=10) == SHAPE and t(M=-1) == SHAPE
+    assert t(dy=X + 4) == ALIGN and at(y=Y + 8) == ALIGN and ats(u=U + 4) == ALIGN
+    assert t(f=0x1) == DTYPE and at(f=0x4) == DTYPE and ats(f=ACC | 0x1) == DTYPE
+    assert t(y=X) == ALIAS and at(y=W + 64) == ALIAS and ats(y=U) == ALIAS
+    assert t(c=lib.gemm_bwd_num_configs()) == CONFIG
+    # M (the contraction of matmul_at) is unrestricted; empty outputs are no-ops
+    assert t(M=0) == 0 and at(K=0) == 0 and at(N=0) == 0
+    n = lib.gemm_bwd_num_configs()
+    assert n >= 1 and all(lib.gemm_bwd_config_name(i) for i in range(n))
+    assert lib.gemm_bwd_config_name(n) is None

@@ -13,6 +13,7 @@ import os
 import torch
 
 GEMM_FLAG_W_F16 = 0x1
+GEMM_FLAG_ACC = 0x2
 GEMM_W_F32 = 0
 GEMM_W_F16 = 1
 
@@ -22,6 +23,8 @@ _lib = None
 EXPORTED = (
     "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_cfg", "gemm_fwd_swiglu_cfg",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
+    "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
+    "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name",
 )
 
 
@@ -65,6 +68,15 @@ def load_library():
     lib.gemm_select_config.restype = c_int
     lib.gemm_status_string.argtypes = [c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
+    for name, n_in in (("gemm_matmul_t", 2), ("gemm_matmul_at", 2), ("gemm_matmul_at_swiglu_a", 3)):
+        getattr(lib, name).argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, p]
+        getattr(lib, name).restype = c_int
+        getattr(lib, name + "_cfg").argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, c_int, p]
+        getattr(lib, name + "_cfg").restype = c_int
+    lib.gemm_bwd_num_configs.argtypes = []
+    lib.gemm_bwd_num_configs.restype = c_int
+    lib.gemm_bwd_config_name.argtypes = [c_int]
+    lib.gemm_bwd_config_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -79,6 +91,15 @@ def num_configs() -> int:
 
 def config_name(config: int):
     name = load_library().gemm_config_name(int(config))
+    return None if name is None else name.decode()
+
+
+def bwd_num_configs() -> int:
+    return load_library().gemm_bwd_num_configs()
+
+
+def bwd_config_name(config: int):
+    name = load_library().gemm_bwd_config_name(int(config))
     return None if name is None else name.decode()
 
 
@@ -184,4 +205,80 @@ def matmul_residual_swiglu_a(G, U, W, R, out=None, config=None):
                          M, K, N, w_dtype, _stream(device), -1 if config is None else config)
     if st != 0:
         raise GemmError(st, "gemm_fwd_swiglu")
+    return out
+
+
+# --- backward linear family (matmul_t, matmul_at and their _acc / _swiglu_a forms) ---
+
+def _bwd_call(name, ptrs, M, K, N, acc, device, config):
+    lib = load_library()
+    flags = GEMM_FLAG_ACC if acc else 0
+    if config is None or config < 0:
+        st = getattr(lib, name)(*ptrs, M, K, N, flags, _stream(device))
+    else:
+        st = getattr(lib, name + "_cfg")(*ptrs, M, K, N, flags, int(config), _stream(device))
+    if st != 0:
+        raise GemmError(st, name)
+
+
+def _out(out, shape, device, acc):
+    if out is None:
+        if acc:
+            raise ValueError("accumulation needs the output tensor")
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _check_act(out, "out", shape, device)
+    return out
+
+
+def matmul_t(dY, W, out=None, acc=False, config=None):
+    """dX = dY @ W^T (matmul_t), or out += dY @ W^T with acc=True (matmul_t_acc).
+    dY [M, N] f32, W [K, N] f32 (the forward's weight); dX [M, K]."""
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise TypeError("dY must be a 2-D torch.Tensor [M, N]")
+    M, N = dY.shape
+    device = dY.device
+    _check_act(dY, "dY", (M, N), device)
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise TypeError("W must be a 2-D torch.Tensor [K, N]")
+    K = W.shape[0]
+    _check_act(W, "W", (K, N), device)
+    out = _out(out, (M, K), device, acc)
+    _bwd_call("gemm_matmul_t", (dY.data_ptr(), W.data_ptr(), out.data_ptr()), M, K, N, acc, device, config)
+    return out
+
+
+def matmul_at(X, dY, out=None, acc=False, config=None):
+    """dW = X^T @ dY (matmul_at), or out += X^T @ dY with acc=True (matmul_at_acc).
+    X [M, K] f32, dY [M, N] f32; dW [K, N]."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise TypeError("X must be a 2-D torch.Tensor [M, K]")
+    M, K = X.shape
+    device = X.device
+    _check_act(X, "X", (M, K), device)
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise TypeError("dY must be a 2-D torch.Tensor [M, N]")
+    N = dY.shape[1]
+    _check_act(dY, "dY", (M, N), device)
+    out = _out(out, (K, N), device, acc)
+    _bwd_call("gemm_matmul_at", (X.data_ptr(), dY.data_ptr(), out.data_ptr()), M, K, N, acc, device, config)
+    return out
+
+
+def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None):
+    """dW = (silu(G) * U)^T @ dY (matmul_at_swiglu_a), or out += ... with acc=True
+    (matmul_at_acc_swiglu_a); the combine is recomputed as A is staged.
+    G, U [M, K] f32, dY [M, N] f32; dW [K, N]."""
+    if not isinstance(G, torch.Tensor) or G.dim() != 2:
+        raise TypeError("G must be a 2-D torch.Tensor [M, K]")
+    M, K = G.shape
+    device = G.device
+    _check_act(G, "G", (M, K), device)
+    _check_act(U, "U", (M, K), device)
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise TypeError("dY must be a 2-D torch.Tensor [M, N]")
+    N = dY.shape[1]
+    _check_act(dY, "dY", (M, N), device)
+    out = _out(out, (K, N), device, acc)
+    _bwd_call("gemm_matmul_at_swiglu_a", (G.data_ptr(), U.data_ptr(), dY.data_ptr(), out.data_ptr()),
+              M, K, N, acc, device, config)
     return out

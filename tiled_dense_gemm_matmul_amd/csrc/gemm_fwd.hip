@@ -229,7 +229,17 @@ struct StageRegs {
     typename std::conditional<W16, f16x4, f32x4>::type b[B_IT > 0 ? B_IT : 1];
 };
 
-template <class C, bool SWIGLU, bool W16, bool RESID>
+// Operand layouts.  kOpNN: A [M x K] and B [K x N], both row-major (the
+// forward products).  kOpNT: B is given as its transpose, [N x K] row-major
+// (matmul_t, dX = dY W^T with the forward W [K x N]).  kOpTN: A is given as
+// its transpose, [K x M] row-major (matmul_at, dW = X^T dY).  A transposed
+// operand is staged the way the other operand's natural layout is: the LDS
+// tile of an operand is always either contraction-contiguous (swizzled rows,
+// one 16-byte read per MFMA fragment) or output-contiguous (padded rows, four
+// reads per fragment), whichever its memory layout makes a plain copy.
+constexpr int kOpNN = 0, kOpNT = 1, kOpTN = 2;
+
+template <class C, bool SWIGLU, bool W16, bool RESID, int OP = kOpNN>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK;
     constexpr int WM = C::WM, WN = C::WN, WK = C::WK;
@@ -239,13 +249,24 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 16, TN = WTN / 16;
     constexpr int CH = BK / 16;             // 16-wide k slices per stage
+    constexpr bool AT = OP == kOpTN, BT = OP == kOpNT;
+    static_assert(!(BT && W16), "a transposed B is fp32");
+    static_assert(!(SWIGLU && OP == kOpNT), "the SwiGLU operand is A");
     constexpr int A_F4 = BM * SL;           // float4s of A per stage
-    constexpr int A_IT = (A_F4 + NS - 1) / NS;
+    constexpr int MQ = BM / 4;              // transposed A: float4s per row of the tile
+    constexpr int A_MB = BK * MQ;
+    constexpr int A_ITEMS = AT ? A_MB : A_F4;
+    constexpr int A_IT = (A_ITEMS + NS - 1) / NS;
     constexpr int NQ = BN / 4;              // float4s per W row in the tile
     constexpr int B_MB = BK * NQ;           // W items (row x 4 columns) per stage
-    constexpr int B_IT = (B_MB + NS - 1) / NS;
+    constexpr int B_F4 = BN * SL;           // transposed B: float4s per stage
+    constexpr int B_ITEMS = BT ? B_F4 : B_MB;
+    constexpr int B_IT = (B_ITEMS + NS - 1) / NS;
+    constexpr int ASTR = BM + 4;            // padded LDS row of a transposed A tile (floats)
     constexpr int BSTR = BN + 4;            // padded LDS row of the W tile (floats)
-    constexpr int STAGE = BM * BK + BK * BSTR;  // floats per LDS stage
+    constexpr int A_LDS = AT ? BK * ASTR : BM * BK;  // floats of the A tile
+    constexpr int B_LDS = BT ? BN * BK : BK * BSTR;
+    constexpr int STAGE = A_LDS + B_LDS;    // floats per LDS stage
     constexpr int CSTR = BN + 4;            // padded row of the output tile in LDS
     constexpr int CTILE = WK * BM * CSTR;   // floats for the output tile(s) in LDS
     static_assert(C::DMA == 0 || C::PF >= 2, "LDS-destination staging needs two register sets");
@@ -282,36 +303,56 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     const int rows_valid = min(BM, M - m0);
     // The A (and UP) resources of a stage start at column k0 of the tile's
     // first row and end with its last valid row, so rows >= M read as 0.
-    const float *Abase = p.A + (size_t)m0 * K;
-    const float *Ubase = SWIGLU ? p.U + (size_t)m0 * K : Abase;
-    const int abytes = rows_valid * K * 4;
-    const char *Wbase = static_cast<const char *>(p.W) + (size_t)n0 * WBYTES;
+    // A transposed operand starts at column m0 (A) or row n0 (B) instead.
+    const float *Abase = AT ? p.A + m0 : p.A + (size_t)m0 * K;
+    const float *Ubase = SWIGLU ? (AT ? p.U + m0 : p.U + (size_t)m0 * K) : Abase;
+    const int abytes = AT ? 0 : rows_valid * K * 4;
+    const char *Wbase = static_cast<const char *>(p.W) + (BT ? (size_t)n0 * K * 4 : (size_t)n0 * WBYTES);
+    const int bbytes = BT ? min(BN, N - n0) * K * 4 : 0;   // transposed B: the tile's valid rows
 
     // Per-thread staging coordinates (fixed over the K loop).
     int a_off[A_IT], a_gk[A_IT];
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
         const int f = stid + i * NS;
-        const int row = f / SL, slot = f % SL;
-        a_gk[i] = (A_IT * NS == A_F4 || f < A_F4) ? slot * 4 : K;  // out-of-range f: always masked
-        a_off[i] = (row * K + slot * 4) * 4;
+        if constexpr (AT) {
+            // rows k of the stage, 4 columns each; columns >= M and padding
+            // items read out of range, rows past the K range fall outside
+            // the stage's resource
+            const int k = f / MQ, mq = f % MQ;
+            const bool live = (A_IT * NS == A_MB || f < A_MB) && (m0 + mq * 4 < M);
+            a_off[i] = live ? (k * M + mq * 4) * 4 : kOOB;
+            a_gk[i] = 0;
+        } else {
+            const int row = f / SL, slot = f % SL;
+            a_gk[i] = (A_IT * NS == A_F4 || f < A_F4) ? slot * 4 : K;  // out-of-range f: always masked
+            a_off[i] = (row * K + slot * 4) * 4;
+        }
     }
     // W items: consecutive staging threads take consecutive 4-column groups
     // of a row, so each load instruction reads contiguous memory.  Rows past
     // the K range fall outside the stage's W resource, so only items outside
     // the tile (columns >= N, padding items) need the kOOB offset.
-    int b_off[B_IT];
+    int b_off[B_IT], b_gk[BT ? B_IT : 1];
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
         const int mb = stid + i * NS;
-        const int k = mb / NQ, nq = mb % NQ;
-        const bool live = (B_IT * NS == B_MB || mb < B_MB) && (n0 + nq * 4 < N);
-        b_off[i] = live ? (k * N + nq * 4) * WBYTES : kOOB;
+        if constexpr (BT) {
+            // as A: rows n of the tile, 4 consecutive k each; rows >= N fall
+            // outside the resource, k past the K range is masked per stage
+            const int row = mb / SL, slot = mb % SL;
+            b_gk[i] = (B_IT * NS == B_F4 || mb < B_F4) ? slot * 4 : K;
+            b_off[i] = (row * K + slot * 4) * 4;
+        } else {
+            const int k = mb / NQ, nq = mb % NQ;
+            const bool live = (B_IT * NS == B_MB || mb < B_MB) && (n0 + nq * 4 < N);
+            b_off[i] = live ? (k * N + nq * 4) * WBYTES : kOOB;
+        }
     }
 
     // Operands staged by LDS-destination loads, and the register items left.
-    constexpr bool DMA_A = (C::DMA & 1) && !SWIGLU && SPEC;
-    constexpr bool DMA_W = (C::DMA & 2) && !W16 && SPEC;
+    constexpr bool DMA_A = (C::DMA & 1) && !SWIGLU && SPEC && !AT;
+    constexpr bool DMA_W = (C::DMA & 2) && !W16 && SPEC && !BT;
     constexpr int A_RIT = DMA_A ? 0 : A_IT;
     constexpr int B_RIT = DMA_W ? 0 : B_IT;
     constexpr int REG_LOADS = A_RIT * (SWIGLU ? 2 : 1) + B_RIT;  // register loads per stage
@@ -368,7 +409,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             for (int j = 0; j < W_DIT; ++j) {
                 const int c = pw + j * NPW;
                 if (W_CH % NPW != 0 && c >= W_CH) break;
-                load_f32x4_to_lds(rW, S + BM * BK + c * 256, wd_off[j]);
+                load_f32x4_to_lds(rW, S + A_LDS + c * 256, wd_off[j]);
             }
         }
         // keep the register loads that follow behind these in issue order, so
@@ -385,35 +426,54 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         // per stage only scalar work moves the resources; per item the A
         // column is checked against the K range (one compare, one select)
         const int krem = kend - k0;
-        const int arem = abytes - k0 * 4;
-        const Rsrc rA = make_rsrc(Abase + k0, arem > 0 ? arem : 0);
-        const Rsrc rU = SWIGLU ? make_rsrc(Ubase + k0, arem > 0 ? arem : 0) : rA;
+        if constexpr (AT) {
+            // rows k0 .. k0+BK-1 of the transposed A, from column m0
+            const int tbytes = krem > 0 ? min(krem, BK) * M * 4 : 0;
+            const Rsrc rA = make_rsrc(Abase + (size_t)k0 * M, tbytes);
+            const Rsrc rU = SWIGLU ? make_rsrc(Ubase + (size_t)k0 * M, tbytes) : rA;
 #pragma unroll
-        for (int i = 0; i < A_RIT; ++i) {
-            const int off = a_gk[i] < krem ? a_off[i] : kOOB;
-            r.a[i] = load_f32x4(rA, off);
-            if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, off);
+            for (int i = 0; i < A_RIT; ++i) {
+                r.a[i] = load_f32x4(rA, a_off[i]);
+                if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, a_off[i]);
+            }
+        } else {
+            const int arem = abytes - k0 * 4;
+            const Rsrc rA = make_rsrc(Abase + k0, arem > 0 ? arem : 0);
+            const Rsrc rU = SWIGLU ? make_rsrc(Ubase + k0, arem > 0 ? arem : 0) : rA;
+#pragma unroll
+            for (int i = 0; i < A_RIT; ++i) {
+                const int off = a_gk[i] < krem ? a_off[i] : kOOB;
+                r.a[i] = load_f32x4(rA, off);
+                if constexpr (SWIGLU) r.u[i] = load_f32x4(rU, off);
+            }
         }
         // W rows k0 .. k0+BK-1 from a resource based at row k0 that ends at
         // the K range, so offsets stay 32-bit whatever K * N is and rows past
         // the range read as 0.
-        const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
-                                  krem > 0 ? min(krem, BK) * N * WBYTES : 0);
+        if constexpr (BT) {
+            // the tile's valid rows of the transposed B, from column k0
+            const int brem = bbytes - k0 * 4;
+            const Rsrc rB = make_rsrc(reinterpret_cast<const float *>(Wbase) + k0, brem > 0 ? brem : 0);
 #pragma unroll
-        for (int i = 0; i < B_RIT; ++i) {
-            if constexpr (W16) r.b[i] = load_f16x4(rW, b_off[i]);
-            else r.b[i] = load_f32x4(rW, b_off[i]);
+            for (int i = 0; i < B_RIT; ++i) r.b[i] = load_f32x4(rB, b_gk[i] < krem ? b_off[i] : kOOB);
+        } else {
+            const Rsrc rW = make_rsrc(Wbase + (size_t)k0 * N * WBYTES,
+                                      krem > 0 ? min(krem, BK) * N * WBYTES : 0);
+#pragma unroll
+            for (int i = 0; i < B_RIT; ++i) {
+                if constexpr (W16) r.b[i] = load_f16x4(rW, b_off[i]);
+                else r.b[i] = load_f32x4(rW, b_off[i]);
+            }
         }
     };
 
     auto store_stage = [&](const Regs &r, int buf) {
         float *As = lds + buf * STAGE;
-        float *Bs = As + BM * BK;
+        float *Bs = As + A_LDS;
 #pragma unroll
         for (int i = 0; i < A_RIT; ++i) {
             const int f = stid + i * NS;
-            if (A_IT * NS != A_F4 && f >= A_F4) continue;
-            const int row = f / SL, slot = f % SL;
+            if (A_IT * NS != A_ITEMS && f >= A_ITEMS) continue;
             f32x4 v = r.a[i];
             if constexpr (SWIGLU) {
                 v.x = silu_mul(v.x, r.u[i].x);
@@ -421,12 +481,23 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 v.z = silu_mul(v.z, r.u[i].z);
                 v.w = silu_mul(v.w, r.u[i].w);
             }
-            *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
+            if constexpr (AT) {
+                const int k = f / MQ, mq = f % MQ;
+                *reinterpret_cast<f32x4 *>(As + k * ASTR + mq * 4) = v;
+            } else {
+                const int row = f / SL, slot = f % SL;
+                *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_RIT; ++i) {
             const int mb = stid + i * NS;
-            if (B_IT * NS != B_MB && mb >= B_MB) continue;
+            if (B_IT * NS != B_ITEMS && mb >= B_ITEMS) continue;
+            if constexpr (BT) {
+                const int row = mb / SL, slot = mb % SL;
+                *reinterpret_cast<f32x4 *>(Bs + (row * SL + (slot ^ swz(row))) * 4) = r.b[i];
+                continue;
+            }
             const int k = mb / NQ, nq = mb % NQ;
             f32x4 t;
             if constexpr (W16) {
@@ -448,22 +519,32 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     const int r16 = lane & 15, q4 = lane >> 4;
     auto compute_stage = [&](int buf) {
         const float *As = lds + buf * STAGE;
-        const float *Bs = As + BM * BK;
+        const float *Bs = As + A_LDS;
 #pragma unroll
         for (int c = wk; c < CH; c += WK) {
             const int slot = c * 4 + q4;
             f32x4 af[TM], bf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 16 + r16;
-                af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4);
+                if constexpr (AT) {
+                    const float *a = As + (c * 16 + q4 * 4) * ASTR + wm * WTM + i * 16 + r16;
+                    af[i] = f32x4{a[0], a[ASTR], a[2 * ASTR], a[3 * ASTR]};
+                } else {
+                    const int row = wm * WTM + i * 16 + r16;
+                    af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4);
+                }
             }
             // W is N-major in LDS: the four k of a lane are four rows; the row
             // padding puts rows k and k+4 sixteen banks apart.
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const float *b = Bs + (c * 16 + q4 * 4) * BSTR + wn * WTN + j * 16 + r16;
-                bf[j] = f32x4{b[0], b[BSTR], b[2 * BSTR], b[3 * BSTR]};
+                if constexpr (BT) {
+                    const int row = wn * WTN + j * 16 + r16;
+                    bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (row * SL + (slot ^ swz(row))) * 4);
+                } else {
+                    const float *b = Bs + (c * 16 + q4 * 4) * BSTR + wn * WTN + j * 16 + r16;
+                    bf[j] = f32x4{b[0], b[BSTR], b[2 * BSTR], b[3 * BSTR]};
+                }
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -479,7 +560,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             // before it, so LDS latency hides behind matrix work instead of
             // stalling in front of every few MFMAs.
             constexpr int NCH = CH / WK;
-            constexpr int DS = TM + 2 * TN;     // b128 per A fragment, two read2_b32 per W fragment
+            // b128 per contraction-contiguous fragment, two read2_b32 per other
+            constexpr int DS = (AT ? 2 * TM : TM) + (BT ? TN : 2 * TN);
             constexpr int MF = 4 * TM * TN;
             constexpr int PER = (MF + DS - 1) / DS;
             __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
@@ -850,6 +932,30 @@ const ConfigEntry kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
+// The backward products use the configurations that the forward selection
+// picks from, under the same names: fn[op == kOpTN][swiglu][accumulate].
+// matmul_t (kOpNT) has no SwiGLU form.
+template <class C>
+constexpr ConfigEntry make_bwd_entry(const char *name) {
+    return ConfigEntry{name, C::BM, C::BN, C::BK, C::NT, C::KS,
+                       {{{gemm_fwd_kernel<C, false, false, false, kOpNT>, gemm_fwd_kernel<C, false, false, true, kOpNT>},
+                         {nullptr, nullptr}},
+                        {{gemm_fwd_kernel<C, false, false, false, kOpTN>, gemm_fwd_kernel<C, false, false, true, kOpTN>},
+                         {gemm_fwd_kernel<C, true, false, false, kOpTN>, gemm_fwd_kernel<C, true, false, true, kOpTN>}}}};
+}
+
+const ConfigEntry kBwdConfigs[] = {
+    make_bwd_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_il_dA"),
+    make_bwd_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
+    make_bwd_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1>>("64x64x64_w2x2_sp4"),
+    make_bwd_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+    make_bwd_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
+    make_bwd_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
+    make_bwd_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
+    make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+};
+constexpr int kNumBwdConfigs = sizeof(kBwdConfigs) / sizeof(kBwdConfigs[0]);
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split-K calls use the static workspace: the whole M x N output must fit a
@@ -860,14 +966,15 @@ bool split_fits(const ConfigEntry &e, int64_t M, int64_t N) {
 
 std::atomic<unsigned> g_region_ticket{0};
 
-int config_index(const char *name) {
-    for (int i = 0; i < kNumConfigs; ++i) {
-        const char *a = kConfigs[i].name, *b = name;
+int table_index(const ConfigEntry *table, int count, const char *name) {
+    for (int i = 0; i < count; ++i) {
+        const char *a = table[i].name, *b = name;
         while (*a && *a == *b) ++a, ++b;
         if (*a == 0 && *b == 0) return i;
     }
     return -1;
 }
+int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, name); }
 
 // Tile choice from the output grid, measured on MI355X: the largest tile
 // that still gives every CU work for the whole kernel, then narrower tiles
@@ -971,6 +1078,65 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// The backward products (public shapes: dY [M x N], W [K x N], X / GATE / UP
+// [M x K]):
+//   op kOpNT, matmul_t:  dX [M x K] (+)= dY W^T   -> kernel (M, K = N, N = K)
+//   op kOpTN, matmul_at: dW [K x N] (+)= A^T dY   -> kernel (M = K, K = M, N)
+// with A = X, or silu(GATE) * UP.  `acc` adds the product to the output's
+// current contents.
+int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B, float *Y, int64_t M,
+            int64_t K, int64_t N, bool acc, int config, void *stream) {
+    const int64_t lim = (int64_t)1 << 31;
+    if (M < 0 || K < 0 || N < 0 || M >= lim || K >= lim || N >= lim) return GEMM_ERR_SHAPE;
+    const bool mk = M > 0 && K > 0, kn = K > 0 && N > 0, mn = M > 0 && N > 0;
+    const bool a_null = op == kOpNT ? (mn && A == nullptr) : (mk && (A == nullptr || (swiglu && U == nullptr)));
+    const bool b_null = op == kOpNT ? (kn && B == nullptr) : (mn && B == nullptr);
+    const bool y_null = op == kOpNT ? (mk && Y == nullptr) : (kn && Y == nullptr);
+    if (a_null || b_null || y_null) return GEMM_ERR_NULL;
+    if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
+    if (K * 1024 >= lim || N * 1024 >= lim) return GEMM_ERR_SHAPE;
+    if (config >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
+    if ((A && !aligned(A, 16)) || (U && !aligned(U, 16)) || (B && !aligned(B, 16)) || (Y && !aligned(Y, 16)))
+        return GEMM_ERR_ALIGN;
+    const size_t abytes = (size_t)(op == kOpNT ? M * N : M * K) * 4;
+    const size_t bbytes = (size_t)(op == kOpNT ? K * N : M * N) * 4;
+    const size_t ybytes = (size_t)(op == kOpNT ? M * K : K * N) * 4;
+    if (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, U, abytes) || overlaps(Y, ybytes, B, bbytes))
+        return GEMM_ERR_ALIAS;
+    // kernel dimensions: output rows, contraction, output columns
+    const int64_t km = op == kOpNT ? M : K, kk = op == kOpNT ? N : M, kn2 = op == kOpNT ? K : N;
+    if (km == 0 || kn2 == 0) return GEMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kk == 0) {
+        if (acc) return GEMM_OK;  // nothing to add
+        const int64_t count = km * kn2;
+        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, nullptr, Y, count);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    int cfg = config;
+    if (cfg < 0) {
+        const int f = select_config(km, kk, kn2, swiglu, 0);
+        cfg = f < 0 ? -1 : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    }
+    if (cfg < 0 || cfg >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
+    const ConfigEntry &e = kBwdConfigs[cfg];
+    if (e.ks > 1 && !split_fits(e, km, kn2)) return GEMM_ERR_CONFIG;
+    Params p;
+    p.A = A; p.U = U; p.W = B; p.R = acc ? Y : nullptr; p.Y = Y;
+    p.M = (int)km; p.K = (int)kk; p.N = (int)kn2;
+    p.tiles_m = (int)ceil_div(km, e.bm);
+    p.tiles_n = (int)ceil_div(kn2, e.bn);
+    p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
+    p.kchunk = (int)(ceil_div(ceil_div(kk, e.ks), e.bk) * e.bk);
+    p.region = e.ks > 1 ? (int)(g_region_ticket.fetch_add(1u, std::memory_order_relaxed) % kSkRegions) : 0;
+    const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
+    if (blocks >= lim) return GEMM_ERR_SHAPE;
+    KernelFn fn = e.fn[op == kOpTN ? 1 : 0][swiglu ? 1 : 0][acc ? 1 : 0];
+    if (fn == nullptr) return GEMM_ERR_DTYPE;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, p);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1007,6 +1173,40 @@ int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, con
                           void *stop) {
     if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
     return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, config, stream, start, stop);
+}
+
+int gemm_matmul_t_cfg(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                      int config, void *stream) {
+    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
+    return run_bwd(kOpNT, false, dY, nullptr, W, dX, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+}
+int gemm_matmul_t(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                  void *stream) {
+    return gemm_matmul_t_cfg(dY, W, dX, M, K, N, flags, -1, stream);
+}
+int gemm_matmul_at_cfg(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                       int config, void *stream) {
+    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
+    return run_bwd(kOpTN, false, X, nullptr, dY, dW, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+}
+int gemm_matmul_at(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                   void *stream) {
+    return gemm_matmul_at_cfg(X, dY, dW, M, K, N, flags, -1, stream);
+}
+int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
+                                int64_t K, int64_t N, uint32_t flags, int config, void *stream) {
+    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
+    return run_bwd(kOpTN, true, GATE, UP, dY, dW, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+}
+int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M, int64_t K,
+                            int64_t N, uint32_t flags, void *stream) {
+    return gemm_matmul_at_swiglu_a_cfg(GATE, UP, dY, dW, M, K, N, flags, -1, stream);
+}
+
+int gemm_bwd_num_configs(void) { return kNumBwdConfigs; }
+
+const char *gemm_bwd_config_name(int config) {
+    return (config >= 0 && config < kNumBwdConfigs) ? kBwdConfigs[config].name : nullptr;
 }
 
 int gemm_num_configs(void) { return kNumConfigs; }

@@ -117,3 +117,23 @@ def random_case(seed, M, K, N, *, swiglu=False, w16=False, residual=False,
     if residual:
         out["R"] = act((M, N))
     return out
+
+
+def backward_case(seed, M, K, N, *, swiglu=False, acc=False, gate_scale=1.0):
+    """A seeded case for the backward products (forward names: M rows, K
+    inputs, N outputs): X [M, K] (or GATE and UP), the forward weight W [K, N],
+    the output gradient dY [M, N], and, for the accumulating forms, previous
+    output contents dX0 [M, K] and dW0 [K, N]."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    if swiglu:
+        out["G"] = _normal(rng, (M, K)) * np.float32(gate_scale)
+        out["U"] = _normal(rng, (M, K))
+    else:
+        out["X"] = _normal(rng, (M, K))
+    out["W"] = _weight(rng, (K, N))
+    out["dY"] = _normal(rng, (M, N))
+    if acc:
+        out["dX0"] = _normal(rng, (M, K))
+        out["dW0"] = _normal(rng, (K, N))
+    return out
