@@ -138,7 +138,7 @@ def time_backward():
             out = t["dX0"].clone() if acc else torch.empty((M, K), device=dev)
             run = lambda: binding.matmul_t(t["dY"], t["W"], out=out, acc=acc)
             ref = lambda: torch.matmul(t["dY"], t["W"].t())
-            kcfg = binding.kernel_config(M, N, K)
+            kcfg = binding.bwd_kernel_config("matmul_t", M, K, N)
         else:
             out = t["dW0"].clone() if acc else torch.empty((K, N), device=dev)
             if "swiglu" in op:
@@ -147,7 +147,7 @@ def time_backward():
             else:
                 run = lambda: binding.matmul_at(t["X"], t["dY"], out=out, acc=acc)
                 ref = lambda: torch.matmul(t["X"].t(), t["dY"])
-            kcfg = binding.kernel_config(K, M, N, swiglu="swiglu" in op)
+            kcfg = binding.bwd_kernel_config("matmul_at", M, K, N, swiglu="swiglu" in op)
 
         def batch(fn, n):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -181,9 +181,12 @@ int gemm_matmul_at_cfg(const float *X, const float *dY, float *dW, int64_t M, in
 int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
                                 int64_t K, int64_t N, uint32_t flags, int config, void *stream);
 
-/* Number and static names of the backward products' configurations. */
+/* Number and static names of the backward products' configurations, and the
+ * one the library picks for a shape (op 1: matmul_t, 2: matmul_at; M, K, N
+ * and swiglu as in the calls above; -1 for an unknown op). */
 int gemm_bwd_num_configs(void);
 const char *gemm_bwd_config_name(int config);
+int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu);
 
 /* Number of tile configurations compiled into the library. */
 int gemm_num_configs(void);

@@ -191,3 +191,15 @@ def test_backward_validation(lib):
     n = lib.gemm_bwd_num_configs()
     assert n >= 1 and all(lib.gemm_bwd_config_name(i) for i in range(n))
     assert lib.gemm_bwd_config_name(n) is None
+
+
+def test_backward_selection(lib):
+    n = lib.gemm_bwd_num_configs()
+    lib.gemm_bwd_select_config.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    for op in (1, 2):
+        for shape in [(512, 768, 768), (512, 3072, 768), (512, 768, 3072), (512, 768, 16384), (8192, 3072, 768),
+                      (1, 4, 4)]:
+            for sw in ((0, 1) if op == 2 else (0,)):
+                assert 0 <= lib.gemm_bwd_select_config(op, *shape, sw) < n, (op, shape, sw)
+    assert lib.gemm_bwd_select_config(0, 512, 768, 768, 0) == -1
+    assert lib.gemm_bwd_select_config(3, 512, 768, 768, 0) == -1

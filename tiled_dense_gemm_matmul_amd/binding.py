@@ -24,7 +24,7 @@ EXPORTED = (
     "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_cfg", "gemm_fwd_swiglu_cfg",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
     "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
-    "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name",
+    "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
 )
 
 
@@ -77,6 +77,8 @@ def load_library():
     lib.gemm_bwd_num_configs.restype = c_int
     lib.gemm_bwd_config_name.argtypes = [c_int]
     lib.gemm_bwd_config_name.restype = ctypes.c_char_p
+    lib.gemm_bwd_select_config.argtypes = [c_int, i64, i64, i64, c_int]
+    lib.gemm_bwd_select_config.restype = c_int
     _lib = lib
     return lib
 
@@ -101,6 +103,13 @@ def bwd_num_configs() -> int:
 def bwd_config_name(config: int):
     name = load_library().gemm_bwd_config_name(int(config))
     return None if name is None else name.decode()
+
+
+def bwd_kernel_config(op, M, K, N, swiglu=False) -> str:
+    """Name of the configuration the library picks for a backward product
+    (op "matmul_t" or "matmul_at"; M, K, N the forward's names)."""
+    code = {"matmul_t": 1, "matmul_at": 2}[op]
+    return bwd_config_name(load_library().gemm_bwd_select_config(code, M, K, N, int(swiglu)))
 
 
 def kernel_config(M, K, N, swiglu=False, w16=False) -> str:

@@ -1009,6 +1009,26 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     return small;
 }
 
+// Tile choice for the backward products, by their kernel dimensions (output
+// rows, contraction, output columns): the forward rule, with two exceptions
+// measured on the seq-512 model's backward shapes.  A transposed A is read
+// with four LDS reads per fragment, so with a short contraction the 64 x 64
+// tiles lose to 32 x 48 tiles with the K range split over four waves (about
+// 20% at 768 x 512 x 3072 and 3072 x 512 x 768).  With a transposed B and a
+// contraction of a few thousand, 16 x 48 tiles with BK = 128 beat the
+// two-workgroup split-K (6% at 512 x 3072 x 768); at 16384 the split wins.
+int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
+    static const int fwd_mid = config_index("64x64x64_w2x2_sp4");
+    static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
+    static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
+    static const int tiny = table_index(kBwdConfigs, kNumBwdConfigs, "16x48x128_k4_sp4_dAW");
+    const int f = select_config(M, K, N, swiglu, 0);
+    if (f < 0) return -1;
+    if (op == kOpTN && f == fwd_mid) return small;
+    if (op == kOpNT && f == fwd_deep_split && K <= 4096) return tiny;
+    return table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+}
+
 // ---------------------------------------------------------------------------
 // validation + launch
 // ---------------------------------------------------------------------------
@@ -1113,11 +1133,7 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
         hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, nullptr, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
-    int cfg = config;
-    if (cfg < 0) {
-        const int f = select_config(km, kk, kn2, swiglu, 0);
-        cfg = f < 0 ? -1 : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
-    }
+    const int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, swiglu);
     if (cfg < 0 || cfg >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
     const ConfigEntry &e = kBwdConfigs[cfg];
     if (e.ks > 1 && !split_fits(e, km, kn2)) return GEMM_ERR_CONFIG;
@@ -1204,6 +1220,12 @@ int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY,
 }
 
 int gemm_bwd_num_configs(void) { return kNumBwdConfigs; }
+
+int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
+    if (op == 1) return select_bwd_config(kOpNT, M, N, K, 0);
+    if (op == 2) return select_bwd_config(kOpTN, K, M, N, swiglu);
+    return -1;
+}
 
 const char *gemm_bwd_config_name(int config) {
     return (config >= 0 && config < kNumBwdConfigs) ? kBwdConfigs[config].name : nullptr;
