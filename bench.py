@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="instead of the step: time the backward products (matmul_t, matmul_at, _acc, "
                          "_swiglu_a) at the seq-512 model's shapes and print a markdown table")
+    ap.add_argument("--loss", action="store_true",
+                    help="instead of the step: time the fused loss (cross_entropy in place, sum_losses) on the "
+                         "seq-512 logits and on the 16 x 512-token batch's, warm and cold, against HBM bandwidth")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the step: run the MFMA ceiling probe (independent fp32 MFMAs only) at 4, 8 "
                          "and 16 waves per CU and print the sustained TFLOP/s and engine clock")
@@ -175,6 +178,75 @@ def time_backward():
         print(json.dumps(row), file=sys.stderr, flush=True)
         lines.append(f"| {label} | {op} [{kcfg}] | {M}×{K}×{N} | {shape_out} | {us:.2f} | {tf:.1f} | "
                      f"{100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f} | {tus:.2f} |")
+    print("\n".join(lines))
+    return rows
+
+
+def time_loss():
+    """cross_entropy over the lm_head logits, each launch timed by its own
+    event pair (median of the launches), warm (logits of the seq-512 step fit
+    the 256 MB Infinity Cache) and cold (a 512 MiB buffer written between
+    launches).  The kernel rewrites the logits in place, so later launches
+    see gradients rather than logits; the work does not depend on the values.
+    Algorithmic bytes: the logits read once and written once, plus targets
+    and losses."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    flush = torch.empty(128 << 20, device=dev)
+    lines = ["| logits S×V | path | warm median µs | warm GB/s | cold median µs | cold GB/s | % of 8 TB/s (cold) | "
+             "sum_losses µs |", "|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for S, V in ((512, 16384), (8192, 50304)):
+        c = inputs.loss_case(S + V, S, V, ignore_every=97)
+        logits = torch.from_numpy(c["logits"]).to(dev)
+        tg = torch.from_numpy(c["targets"].astype(np.int32)).to(dev)
+        losses = torch.empty(S, device=dev)
+        inv = 1.0 / int((c["targets"] < V).sum())
+        lib = binding.load_library()
+        # the C entry point directly, so that the events see only the kernel
+        run = lambda: lib.loss_cross_entropy(logits.data_ptr(), tg.data_ptr(), losses.data_ptr(), S, V, 0.1, 1e-4,
+                                             inv, st.cuda_stream)
+
+        def sample(n, cold):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a, b in evs:
+                if cold:
+                    flush.fill_(1.0)
+                a.record(st)
+                run()
+                b.record(st)
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            run()
+            torch.cuda.synchronize()
+        n = 50 if S * V < 1e8 else 10
+        warm, cold = sample(n, False), sample(n, True)
+        total = torch.empty(1, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(20):
+            lib.loss_sum_losses(losses.data_ptr(), total.data_ptr(), S, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        sl_us = e0.elapsed_time(e1) * 1e3 / 20
+        nbytes = 2 * S * V * 4 + 2 * S * 4
+        path = "registers, 256 threads/row" if V <= 16384 else ("registers, 1024 threads/row" if V <= 65536
+                                                                 else "streaming")
+        row = {"S": S, "V": V, "warm_us": round(warm, 2), "warm_GBps": round(nbytes / warm / 1e3, 1),
+               "cold_us": round(cold, 2), "cold_GBps": round(nbytes / cold / 1e3, 1),
+               "frac_hbm_peak_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4), "sum_losses_us": round(sl_us, 2)}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        lines.append(f"| {S}×{V} | {path} | {warm:.2f} | {nbytes / warm / 1e3:.0f} | {cold:.2f} | "
+                     f"{nbytes / cold / 1e3:.0f} | {100 * nbytes / cold / 1e3 / PEAK_HBM_GBS:.1f} | {sl_us:.2f} |")
+        del logits
+        torch.cuda.empty_cache()
     print("\n".join(lines))
     return rows
 
@@ -549,6 +621,9 @@ def main():
         return
     if args.backward:
         time_backward()
+        return
+    if args.loss:
+        time_loss()
         return
     if args.traffic_from:
         traffic_from(args.traffic_from)

@@ -203,3 +203,27 @@ def test_backward_selection(lib):
                 assert 0 <= lib.gemm_bwd_select_config(op, *shape, sw) < n, (op, shape, sw)
     assert lib.gemm_bwd_select_config(0, 512, 768, 768, 0) == -1
     assert lib.gemm_bwd_select_config(3, 512, 768, 768, 0) == -1
+
+
+def test_loss_exports_and_validation(lib):
+    """include/loss.h: every declared function is exported, and bad arguments
+    are rejected synchronously (fake host pointers, nothing launched)."""
+    with open(os.path.join(ROOT, "include", "loss.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(loss_[a-z_]+)\s*\(", text)))
+    assert names == ["loss_cross_entropy", "loss_sum_losses"]
+    for n in names:
+        assert hasattr(lib, n)
+    NULL, SHAPE, ALIGN = _status("GEMM_ERR_NULL"), _status("GEMM_ERR_SHAPE"), _status("GEMM_ERR_ALIGN")
+    DTYPE, ALIAS = _status("GEMM_ERR_DTYPE"), _status("GEMM_ERR_ALIAS")
+    ce = lambda l=X, t=W, o=Y, S=8, V=64, a=0.0, b=0.0, n=1.0: lib.loss_cross_entropy(l, t, o, S, V, a, b, n, None)
+    assert ce(S=-1) == SHAPE and ce(V=-1) == SHAPE and ce(V=1 << 29) == SHAPE
+    assert ce(l=None) == NULL and ce(t=None) == NULL and ce(o=None) == NULL
+    assert ce(l=X + 2) == ALIGN and ce(t=W + 1) == ALIGN and ce(o=Y + 3) == ALIGN
+    assert ce(a=-0.1) == DTYPE and ce(a=1.5) == DTYPE and ce(b=-1.0) == DTYPE
+    assert ce(b=float("inf")) == DTYPE and ce(n=float("nan")) == DTYPE
+    assert ce(o=X + 64) == ALIAS and ce(o=W) == ALIAS
+    assert ce(S=0) == 0 and ce(S=0, l=None, t=None, o=None) == 0
+    sl = lambda x=X, o=Y, S=8: lib.loss_sum_losses(x, o, S, None)
+    assert sl(S=-1) == SHAPE and sl(o=None) == NULL and sl(x=None) == NULL and sl(x=X + 2) == ALIGN
+    assert sl(o=X + 4) == ALIAS

@@ -1,0 +1,124 @@
+"""The fused loss kernels on the GPU against the oracle (oracle/loss.py):
+cross_entropy (per-row loss, the gradient in place, label smoothing and
+z-loss, ignored rows) in each of its paths (16-byte and 4-byte accesses, 256-
+and 1024-thread register-resident rows, the streaming fallback), at the
+seq-512 model's shape [512 x 16384] in full and at [8192 x 50304] on sampled
+rows, on degenerate shapes, and sum_losses."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import loss as OL
+from tiled_dense_gemm_matmul_amd import inputs
+
+from _gpu import device, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, alpha, beta, inv_norm):
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    logits = to_dev(case["logits"])
+    tg = torch.from_numpy(case["targets"].astype(np.int64)).to(device())
+    losses = binding.cross_entropy(logits, tg, alpha=alpha, beta=beta, inv_norm=inv_norm)
+    torch.cuda.synchronize()
+    return losses.cpu().numpy(), logits
+
+
+def check(case, losses, grad, alpha, beta, inv_norm, rows=None, label=""):
+    import oracle
+    loss_ref, dl_ref, mag = OL.cross_entropy(case["logits"], case["targets"], alpha=alpha, beta=beta,
+                                            inv_norm=inv_norm, rows=rows)
+    sel = slice(None) if rows is None else rows
+    r1 = oracle.compare(losses[sel], loss_ref, mag["loss"], OL.TOL_LOSS)
+    r2 = oracle.compare(grad[sel], dl_ref, mag["dlogits"], OL.TOL_DLOGITS)
+    say(f"  {label}: loss max err/tol {r1['max_ratio']:.3g} fails {r1['fails']}; "
+        f"dlogits max err/tol {r2['max_ratio']:.3g} fails {r2['fails']} of {r2['n']}")
+    assert r1["fails"] == 0 and r2["fails"] == 0, (r1, r2)
+
+
+PARAMS = [(0.0, 0.0), (0.1, 1e-4), (0.05, 0.0), (0.0, 0.01)]
+
+
+@pytest.mark.parametrize("alpha,beta", PARAMS)
+def test_seq512_full(alpha, beta):
+    S, V = 512, 16384
+    say(f"cross_entropy S={S} V={V} alpha={alpha} beta={beta}")
+    case = inputs.loss_case(7, S, V, ignore_every=17)
+    inv = 1.0 / int((case["targets"] < V).sum())
+    losses, grad = run(case, alpha, beta, inv)
+    check(case, losses, grad.cpu().numpy(), alpha, beta, inv, label=f"{S}x{V}")
+
+
+@pytest.mark.parametrize("S,V", [(40, 1001), (9, 3), (5, 1), (12, 20001), (6, 70000), (16, 65536), (33, 50304),
+                                 (7, 16388)])
+def test_paths_and_ragged_vocab(S, V):
+    say(f"cross_entropy S={S} V={V}")
+    case = inputs.loss_case(S * 31 + V, S, V, scale=3.0, ignore_every=5)
+    for alpha, beta in [(0.0, 0.0), (0.1, 1e-3)]:
+        losses, grad = run(case, alpha, beta, 0.125)
+        check(case, losses, grad.cpu().numpy(), alpha, beta, 0.125, label=f"{S}x{V} a={alpha} b={beta}")
+
+
+def test_large_sampled():
+    """The 16 x 512-token batch's logits [8192 x 50304] (1.65 GB), sampled rows
+    (first and last included) against the oracle, every row's gradient sum
+    against 2 beta lse inv_norm, whose z-loss part is zero here."""
+    S, V = 8192, 50304
+    say(f"cross_entropy S={S} V={V} (sampled)")
+    case = inputs.loss_case(11, S, V, ignore_every=101)
+    inv = 1.0 / int((case["targets"] < V).sum())
+    losses, grad = run(case, 0.1, 0.0, inv)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, S - 2, S - 1], rng.choice(S, 28, replace=False)]))
+    g = grad[rows].cpu().numpy()
+    full = np.zeros((S, V), np.float32)
+    full[rows] = g
+    check(case, losses, full, 0.1, 0.0, inv, rows=rows, label="sampled rows")
+    import torch
+    rs = grad.double().sum(dim=1).cpu().numpy()
+    ra = grad.double().abs().sum(dim=1).cpu().numpy()
+    assert np.all(np.abs(rs) <= 1e-5 * ra + 1e-9), float(np.max(np.abs(rs) / (ra + 1e-30)))
+    del grad
+    torch.cuda.empty_cache()
+
+
+def test_ignored_and_degenerate():
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    dev = device()
+    # every row ignored: zero losses and zero gradient
+    case = inputs.loss_case(2, 6, 100)
+    case["targets"][:] = 100
+    losses, grad = run(case, 0.1, 1e-3, 1.0)
+    assert not losses.any() and torch.count_nonzero(grad).item() == 0
+    # V == 0: every row is ignored, nothing to read
+    logits = torch.empty((4, 0), device=dev)
+    out = binding.cross_entropy(logits, torch.zeros(4, dtype=torch.int64, device=dev), inv_norm=1.0)
+    torch.cuda.synchronize()
+    assert out.shape == (4,) and torch.count_nonzero(out).item() == 0
+    # S == 0: nothing
+    assert binding.cross_entropy(torch.empty((0, 8), device=dev), torch.empty(0, dtype=torch.int64, device=dev),
+                                 inv_norm=1.0).shape == (0,)
+    assert float(binding.sum_losses(torch.empty(0, device=dev)).item()) == 0.0
+
+
+def test_sum_losses_and_determinism():
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    case = inputs.loss_case(5, 512, 16384, ignore_every=9)
+    inv = 1.0 / int((case["targets"] < 16384).sum())
+    l1, g1 = run(case, 0.1, 1e-4, inv)
+    l2, g2 = run(case, 0.1, 1e-4, inv)
+    assert np.array_equal(l1, l2) and torch.equal(g1, g2)
+    for S in (1, 512, 4099):
+        x = (np.random.default_rng(S).standard_normal(S) * 10).astype(np.float32)
+        tot = float(binding.sum_losses(to_dev(x)).item())
+        ref = OL.sum_losses(x)
+        assert abs(tot - ref) <= 2 * S * 2.0 ** -24 * float(np.abs(x).sum()), (S, tot, ref)
+    tot = float(binding.sum_losses(to_dev(l1)).item())
+    ref = OL.sum_losses(OL.cross_entropy(case["logits"], case["targets"], 0.1, 1e-4, inv)[0])
+    assert abs(tot - ref) <= 1e-5 * abs(ref) + 1e-4
+    _ = math

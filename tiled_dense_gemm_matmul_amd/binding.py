@@ -25,6 +25,7 @@ EXPORTED = (
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
     "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
     "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
+    "loss_cross_entropy", "loss_sum_losses",
 )
 
 
@@ -79,6 +80,11 @@ def load_library():
     lib.gemm_bwd_config_name.restype = ctypes.c_char_p
     lib.gemm_bwd_select_config.argtypes = [c_int, i64, i64, i64, c_int]
     lib.gemm_bwd_select_config.restype = c_int
+    f32 = ctypes.c_float
+    lib.loss_cross_entropy.argtypes = [p, p, p, i64, i64, f32, f32, f32, p]
+    lib.loss_cross_entropy.restype = c_int
+    lib.loss_sum_losses.argtypes = [p, p, i64, p]
+    lib.loss_sum_losses.restype = c_int
     _lib = lib
     return lib
 
@@ -290,4 +296,54 @@ def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None):
     out = _out(out, (K, N), device, acc)
     _bwd_call("gemm_matmul_at_swiglu_a", (G.data_ptr(), U.data_ptr(), dY.data_ptr(), out.data_ptr()),
               M, K, N, acc, device, config)
+    return out
+
+
+# --- fused loss (include/loss.h) ---
+
+def cross_entropy(logits, targets, alpha=0.0, beta=0.0, inv_norm=None, losses=None):
+    """cross_entropy: per-row losses, and the gradient written over `logits`
+    in place.  logits [S, V] f32, targets [S] int32/int64 (values >= V, or
+    negative, mark ignored rows); inv_norm defaults to 1 / (number of rows
+    with a target in [0, V)), which reads that count back to the host.
+    Returns the losses [S] f32 tensor."""
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise TypeError("logits must be a 2-D torch.Tensor [S, V]")
+    S, V = logits.shape
+    device = logits.device
+    _check_act(logits, "logits", (S, V), device)
+    if not isinstance(targets, torch.Tensor) or tuple(targets.shape) != (S,) or targets.device != device:
+        raise ValueError(f"targets must be a [{S}] tensor on {device}")
+    if targets.dtype not in (torch.int32, torch.int64):
+        raise TypeError("targets must be int32 or int64")
+    # the kernel reads targets as uint32: a negative value reads as >= V and
+    # marks an ignored row, like any other out-of-range target
+    t32 = targets if targets.dtype == torch.int32 and targets.is_contiguous() else targets.to(torch.int32).contiguous()
+    if inv_norm is None:
+        valid = int(((targets >= 0) & (targets < V)).sum().item())
+        inv_norm = 1.0 / valid if valid else 0.0
+    if losses is None:
+        losses = torch.empty((S,), dtype=torch.float32, device=device)
+    else:
+        _check_act(losses, "losses", (S,), device)
+    st = load_library().loss_cross_entropy(logits.data_ptr(), t32.data_ptr(), losses.data_ptr(), S, V,
+                                           float(alpha), float(beta), float(inv_norm), _stream(device))
+    if st != 0:
+        raise GemmError(st, "loss_cross_entropy")
+    return losses
+
+
+def sum_losses(losses, out=None):
+    """sum_losses: the scalar total of the per-row losses, as a [1] tensor."""
+    if not isinstance(losses, torch.Tensor) or losses.dim() != 1:
+        raise TypeError("losses must be a 1-D torch.Tensor")
+    device = losses.device
+    _check_act(losses, "losses", tuple(losses.shape), device)
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=device)
+    else:
+        _check_act(out, "out", (1,), device)
+    st = load_library().loss_sum_losses(losses.data_ptr(), out.data_ptr(), losses.shape[0], _stream(device))
+    if st != 0:
+        raise GemmError(st, "loss_sum_losses")
     return out

@@ -11,6 +11,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gemm_fwd.hip")
+LOSS_SRC = os.path.join(PKG, "csrc", "loss.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemmfwd.so")
 PROBE_SRC = os.path.join(PKG, "csrc", "mfma_probe.hip")
@@ -22,10 +23,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def _hipcc(src: str, lib: str, verbose: bool) -> str:
+def _hipcc(srcs, lib: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = lib + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, src, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -34,13 +35,13 @@ def _hipcc(src: str, lib: str, verbose: bool) -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """The GEMM library (every kernel of the forward family)."""
-    return _hipcc(SRC, LIB, verbose)
+    """The library: the GEMM family (forward and backward) and the fused loss."""
+    return _hipcc([SRC, LOSS_SRC], LIB, verbose)
 
 
 def build_probe(verbose: bool = False) -> str:
     """The MFMA ceiling probe used by bench.py --mfma-ceiling."""
-    return _hipcc(PROBE_SRC, PROBE_LIB, verbose)
+    return _hipcc([PROBE_SRC], PROBE_LIB, verbose)
 
 
 if __name__ == "__main__":

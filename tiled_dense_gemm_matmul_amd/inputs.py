@@ -137,3 +137,15 @@ def backward_case(seed, M, K, N, *, swiglu=False, acc=False, gate_scale=1.0):
         out["dX0"] = _normal(rng, (M, K))
         out["dW0"] = _normal(rng, (K, N))
     return out
+
+
+def loss_case(seed, S, V, *, scale=2.0, ignore_every=0):
+    """A seeded case for the fused loss: logits [S, V] float32 drawn N(0, 1)
+    times `scale`, targets [S] uint32 uniform in [0, V); with ignore_every =
+    k > 0 every k-th row gets the ignored target V (padding)."""
+    rng = np.random.default_rng(seed)
+    logits = _normal(rng, (S, V)) * np.float32(scale)
+    targets = rng.integers(0, max(V, 1), size=S).astype(np.uint32) if V > 0 else np.zeros(S, np.uint32)
+    if ignore_every:
+        targets[::ignore_every] = V
+    return {"logits": logits, "targets": targets}
