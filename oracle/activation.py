@@ -89,18 +89,31 @@ def ffn_gelu_backward(grad_hidden, pre_gelu):
 def _gelu_backward(g, x, pre_gelu):
     inner = SQRT_2_OVER_PI * (x + GELU_COEFF * x ** 3)
     t = np.tanh(inner)
-    mag = np.abs(g) * (0.5 * np.abs(1.0 + t) + 0.5 * np.abs(x) * (1.0 - t * t) * SQRT_2_OVER_PI
-                       * (1.0 + 3.0 * GELU_COEFF * x * x) * (1.0 + np.abs(inner)))
+    d_inner = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_COEFF * x * x)
+    mag = np.abs(g) * (1.0 + np.abs(x) * d_inner) * (1.0 + (1.0 - t * t) * _inner_mag(x))
     return nan_guard(g * gelu_derivative(pre_gelu)), nan_guard(mag)
+
+
+def _inner_mag(x):
+    """|x| + 0.044715 |x|^3, scaled as the tanh argument: the size that the
+    argument's own rounding is relative to."""
+    return SQRT_2_OVER_PI * (np.abs(x) + GELU_COEFF * np.abs(x) ** 3)
 
 
 def gelu_inplace(x):
     """(gelu(x), scale)."""
     x64 = np.asarray(x, dtype=np.float64)
-    return gelu(x64), np.abs(x64) * (1.0 + np.abs(SQRT_2_OVER_PI * np.clip(x64, -100, 100)) * 3.0)
+    xc = np.clip(x64, -100.0, 100.0)
+    t = np.tanh(SQRT_2_OVER_PI * (xc + GELU_COEFF * xc ** 3))
+    return gelu(x64), np.abs(x64) * (1.0 + (1.0 - t * t) * _inner_mag(xc))
 
 
-# |x - x_ref| <= rel * scale + abs: fp32 exp / tanh of arguments up to ~100
-# are good to a few 1e-6 relative; the scales above already carry the
-# cancellation-prone terms by their magnitudes.
+# |x - x_ref| <= rel * scale + abs.  The scales are the magnitudes of the
+# terms before they cancel, not of the result: in fp32 the page's GeLU
+# formulas lose all relative accuracy where tanh(inner) is within an ulp of
+# +-1 (|x| > ~4), because 1 + t and 1 - t^2 cancel; the error there is a few
+# ulps of 0.5 (1 + |t|) and of 0.5 |x| (1 + t^2) d_inner, and the argument's
+# rounding adds sech^2 times a few ulps of |inner|.  Likewise silu' near its
+# zero.  With fp32 exp and tanh good to about 2 ulps, 1e-5 leaves a margin of
+# about ten over the worst case.
 TOL = (1e-5, 1e-30)

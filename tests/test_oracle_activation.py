@@ -95,8 +95,8 @@ def _mutant(**patch):
 MUTANTS = {
     "silu_prime_sign": {"return s * (1.0 + x * (1.0 - s))": "return s * (1.0 - x * (1.0 - s))"},
     "sigmoid_branch": {"e / (1.0 + e))": "1.0 / (1.0 + e))"},
-    "gelu_coeff": {"d_inner = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_COEFF * x * x)":
-                   "d_inner = SQRT_2_OVER_PI * (1.0 + GELU_COEFF * x * x)"},
+    "gelu_coeff": {"sech2 = 1.0 - t * t\n    d_inner = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_COEFF * x * x)":
+                   "sech2 = 1.0 - t * t\n    d_inner = SQRT_2_OVER_PI * (1.0 + GELU_COEFF * x * x)"},
     "grad_up_uses_gate": {"du = nan_guard(g * silu(x))": "du = nan_guard(g * x)"},
     "no_nan_guard": {"return np.where(np.isfinite(x), x, 0.0)": "return x"},
 }
