@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--loss", action="store_true",
                     help="instead of the step: time the fused loss (cross_entropy in place, sum_losses) on the "
                          "seq-512 logits and on the 16 x 512-token batch's, warm and cold, against HBM bandwidth")
+    ap.add_argument("--activation", action="store_true",
+                    help="instead of the step: time the FFN activation kernels (ffn_swiglu_backward, "
+                         "ffn_gelu_backward, gelu_inplace) at the seq-512 and 8192-token hidden sizes")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the step: run the MFMA ceiling probe (independent fp32 MFMAs only) at 4, 8 "
                          "and 16 waves per CU and print the sustained TFLOP/s and engine clock")
@@ -247,6 +250,63 @@ def time_loss():
                      f"{nbytes / cold / 1e3:.0f} | {100 * nbytes / cold / 1e3 / PEAK_HBM_GBS:.1f} | {sl_us:.2f} |")
         del logits
         torch.cuda.empty_cache()
+    print("\n".join(lines))
+    return rows
+
+
+def time_activation():
+    """The FFN activation kernels on their own, each launch timed by its own
+    event pair around the C entry point (median), warm and cold (a 512 MiB
+    buffer written between launches).  Algorithmic bytes per element:
+    ffn_swiglu_backward reads three arrays and writes two (20 B),
+    ffn_gelu_backward reads two and writes one (12 B), gelu_inplace reads
+    and writes one and keeps a copy of the input (12 B)."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    lib = binding.load_library()
+    flush = torch.empty(128 << 20, device=dev)
+    lines = ["| kernel | elements | bytes/elem | warm µs | warm GB/s | cold µs | cold GB/s | % of 8 TB/s (cold) |",
+             "|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for n in (512 * 3072, 8192 * 3072):
+        c = inputs.activation_case(n % 1000 + 1, n)
+        g, x, u = (torch.from_numpy(c[k]).to(dev) for k in ("g", "gate", "up"))
+        o1, o2 = torch.empty_like(g), torch.empty_like(g)
+        kernels = [
+            ("ffn_swiglu_backward", 20, lambda: lib.act_ffn_swiglu_backward(
+                g.data_ptr(), x.data_ptr(), u.data_ptr(), o1.data_ptr(), o2.data_ptr(), n, st.cuda_stream)),
+            ("ffn_gelu_backward", 12, lambda: lib.act_ffn_gelu_backward(
+                g.data_ptr(), x.data_ptr(), o1.data_ptr(), n, st.cuda_stream)),
+            ("gelu_inplace (keeping the input)", 12, lambda: lib.act_gelu_inplace(
+                o2.data_ptr(), o1.data_ptr(), n, st.cuda_stream)),
+        ]
+        for name, bpe, run in kernels:
+            def sample(k, cold):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+                for a, b in evs:
+                    if cold:
+                        flush.fill_(1.0)
+                    a.record(st)
+                    assert run() == 0
+                    b.record(st)
+                torch.cuda.synchronize()
+                return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.2:
+                run()
+                torch.cuda.synchronize()
+            warm, cold = sample(50, False), sample(50, True)
+            nbytes = bpe * n
+            row = {"kernel": name, "n": n, "warm_us": round(warm, 2), "warm_GBps": round(nbytes / warm / 1e3, 1),
+                   "cold_us": round(cold, 2), "cold_GBps": round(nbytes / cold / 1e3, 1),
+                   "frac_hbm_peak_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4)}
+            rows.append(row)
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            lines.append(f"| {name} | {n} | {bpe} | {warm:.2f} | {nbytes / warm / 1e3:.0f} | {cold:.2f} | "
+                         f"{nbytes / cold / 1e3:.0f} | {100 * nbytes / cold / 1e3 / PEAK_HBM_GBS:.1f} |")
     print("\n".join(lines))
     return rows
 
@@ -624,6 +684,9 @@ def main():
         return
     if args.loss:
         time_loss()
+        return
+    if args.activation:
+        time_activation()
         return
     if args.traffic_from:
         traffic_from(args.traffic_from)

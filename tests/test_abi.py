@@ -227,3 +227,21 @@ def test_loss_exports_and_validation(lib):
     sl = lambda x=X, o=Y, S=8: lib.loss_sum_losses(x, o, S, None)
     assert sl(S=-1) == SHAPE and sl(o=None) == NULL and sl(x=None) == NULL and sl(x=X + 2) == ALIGN
     assert sl(o=X + 4) == ALIAS
+
+
+def test_activation_exports_and_validation(lib):
+    with open(os.path.join(ROOT, "include", "activation.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(act_[a-z_]+)\s*\(", text)))
+    assert names == ["act_ffn_gelu_backward", "act_ffn_swiglu_backward", "act_gelu_inplace"]
+    for n in names:
+        assert hasattr(lib, n)
+    NULL, SHAPE, ALIGN, ALIAS = (_status(s) for s in ("GEMM_ERR_NULL", "GEMM_ERR_SHAPE", "GEMM_ERR_ALIGN",
+                                                       "GEMM_ERR_ALIAS"))
+    sw = lambda g=X, x=W, u=U, dg=Y, du=R, n=64: lib.act_ffn_swiglu_backward(g, x, u, dg, du, n, None)
+    assert sw(n=-1) == SHAPE and sw(n=0) == 0 and sw(g=None) == NULL and sw(du=None) == NULL
+    assert sw(x=W + 2) == ALIGN and sw(dg=R) == ALIAS and sw(dg=X + 16) == ALIAS and sw(du=Y + 128) == ALIAS
+    gb = lambda g=X, x=W, d=Y, n=64: lib.act_ffn_gelu_backward(g, x, d, n, None)
+    assert gb(n=-1) == SHAPE and gb(x=None) == NULL and gb(d=Y + 1) == ALIGN and gb(d=W + 4) == ALIAS
+    gi = lambda x=X, p=Y, n=64: lib.act_gelu_inplace(x, p, n, None)
+    assert gi(x=None) == NULL and gi(p=X) == ALIAS and gi(p=X + 8) == ALIAS and gi(n=0) == 0

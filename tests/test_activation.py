@@ -1,0 +1,84 @@
+"""The FFN activation kernels on the GPU against the oracle
+(oracle/activation.py): ffn_swiglu_backward, ffn_gelu_backward and
+gelu_inplace on the seq-512 FFN's hidden size (512 x 3072) and the 16 x
+512-token batch's (8192 x 3072), on ragged lengths that exercise the tail and
+the 4-byte path, with NaN and infinite inputs through nan_guard, and with an
+output that is the very same array as an input."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import activation as OA
+from tiled_dense_gemm_matmul_amd import inputs
+
+from _gpu import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def cmp(label, y, ref, scale):
+    res = oracle.compare(np.asarray(y), ref, scale, OA.TOL)
+    say(f"  {label}: max err/tol {res['max_ratio']:.3g} fails {res['fails']} of {res['n']}")
+    assert res["fails"] == 0, res
+
+
+@pytest.mark.parametrize("n", [512 * 3072, 8192 * 3072, 1, 3, 4097, 100003])
+def test_three_kernels(n):
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    say(f"activation kernels n={n}")
+    c = inputs.activation_case(n % 1000 + 1, n)
+    g, x, u = to_dev(c["g"]), to_dev(c["gate"]), to_dev(c["up"])
+    dg, du = binding.ffn_swiglu_backward(g, x, u)
+    dp = binding.ffn_gelu_backward(g, x)
+    y = x.clone()
+    keep = torch.empty_like(x)
+    binding.gelu_inplace(y, pre_gelu=keep)
+    torch.cuda.synchronize()
+    rdg, rdu, sg, su = OA.ffn_swiglu_backward(c["g"], c["gate"], c["up"])
+    cmp("grad_gate", dg.cpu(), rdg, sg)
+    cmp("grad_up", du.cpu(), rdu, su)
+    rdp, sp = OA.ffn_gelu_backward(c["g"], c["gate"])
+    cmp("grad_pre", dp.cpu(), rdp, sp)
+    ry, sy = OA.gelu_inplace(c["gate"])
+    cmp("gelu", y.cpu(), ry, sy)
+    assert torch.equal(keep, x)
+
+
+def test_misaligned_path_and_in_place_outputs():
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    n = 5000
+    c = inputs.activation_case(9, n + 1)
+    base = {k: to_dev(v) for k, v in c.items()}
+    # views starting one float in: 4-byte aligned only, so the 4-byte path runs
+    g, x, u = base["g"][1:], base["gate"][1:], base["up"][1:]
+    dg, du = binding.ffn_swiglu_backward(g, x, u)
+    rdg, rdu, sg, su = OA.ffn_swiglu_backward(c["g"][1:], c["gate"][1:], c["up"][1:])
+    torch.cuda.synchronize()
+    cmp("grad_gate (4-byte path)", dg.cpu(), rdg, sg)
+    cmp("grad_up (4-byte path)", du.cpu(), rdu, su)
+    # outputs written over the inputs they replace (gate -> grad_gate, up -> grad_up)
+    x2, u2 = to_dev(c["gate"]), to_dev(c["up"])
+    binding.ffn_swiglu_backward(to_dev(c["g"]), x2, u2, grad_gate=x2, grad_up=u2)
+    torch.cuda.synchronize()
+    rdg, rdu, sg, su = OA.ffn_swiglu_backward(c["g"], c["gate"], c["up"])
+    cmp("grad_gate in place", x2.cpu(), rdg, sg)
+    cmp("grad_up in place", u2.cpu(), rdu, su)
+
+
+def test_non_finite_inputs_are_guarded():
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    g = np.array([1.0, np.nan, 2.0, 1.0, np.inf, 1.0, -1.0, 3.0], np.float32)
+    x = np.array([0.5, 0.5, np.nan, np.inf, 0.5, -np.inf, 200.0, -200.0], np.float32)
+    u = np.ones(8, np.float32)
+    dg, du = binding.ffn_swiglu_backward(to_dev(g), to_dev(x), to_dev(u))
+    dp = binding.ffn_gelu_backward(to_dev(g), to_dev(x))
+    torch.cuda.synchronize()
+    rdg, rdu, sg, su = OA.ffn_swiglu_backward(g, x, u)
+    rdp, sp = OA.ffn_gelu_backward(g, x)
+    for name, y, r, s in (("grad_gate", dg, rdg, sg), ("grad_up", du, rdu, su), ("grad_pre", dp, rdp, sp)):
+        y = y.cpu().numpy()
+        assert np.all(np.isfinite(y)), (name, y)
+        cmp(name, y, r, s)

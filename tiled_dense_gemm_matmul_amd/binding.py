@@ -25,7 +25,7 @@ EXPORTED = (
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
     "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
     "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
-    "loss_cross_entropy", "loss_sum_losses",
+    "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward", "act_gelu_inplace",
 )
 
 
@@ -85,6 +85,12 @@ def load_library():
     lib.loss_cross_entropy.restype = c_int
     lib.loss_sum_losses.argtypes = [p, p, i64, p]
     lib.loss_sum_losses.restype = c_int
+    lib.act_ffn_swiglu_backward.argtypes = [p, p, p, p, p, i64, p]
+    lib.act_ffn_swiglu_backward.restype = c_int
+    lib.act_ffn_gelu_backward.argtypes = [p, p, p, i64, p]
+    lib.act_ffn_gelu_backward.restype = c_int
+    lib.act_gelu_inplace.argtypes = [p, p, i64, p]
+    lib.act_gelu_inplace.restype = c_int
     _lib = lib
     return lib
 
@@ -347,3 +353,56 @@ def sum_losses(losses, out=None):
     if st != 0:
         raise GemmError(st, "loss_sum_losses")
     return out
+
+
+# --- FFN activation kernels (include/activation.h) ---
+
+def _same_shape(name, t, ref):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 torch.Tensor")
+    if t.device != ref.device or t.shape != ref.shape:
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)} on {ref.device}")
+
+
+def ffn_swiglu_backward(grad_hidden, gate, up, grad_gate=None, grad_up=None):
+    """grad_gate = nan_guard(g * up * silu'(gate)), grad_up = nan_guard(g * silu(gate)),
+    element-wise over tensors of one shape.  Returns (grad_gate, grad_up)."""
+    _same_shape("grad_hidden", grad_hidden, grad_hidden)
+    _same_shape("gate", gate, grad_hidden)
+    _same_shape("up", up, grad_hidden)
+    grad_gate = torch.empty_like(gate) if grad_gate is None else grad_gate
+    grad_up = torch.empty_like(up) if grad_up is None else grad_up
+    _same_shape("grad_gate", grad_gate, grad_hidden)
+    _same_shape("grad_up", grad_up, grad_hidden)
+    st = load_library().act_ffn_swiglu_backward(grad_hidden.data_ptr(), gate.data_ptr(), up.data_ptr(),
+                                                grad_gate.data_ptr(), grad_up.data_ptr(), grad_hidden.numel(),
+                                                _stream(grad_hidden.device))
+    if st != 0:
+        raise GemmError(st, "act_ffn_swiglu_backward")
+    return grad_gate, grad_up
+
+
+def ffn_gelu_backward(grad_hidden, pre_gelu, grad_pre=None):
+    """grad_pre = nan_guard(g * gelu'(pre_gelu)), element-wise."""
+    _same_shape("grad_hidden", grad_hidden, grad_hidden)
+    _same_shape("pre_gelu", pre_gelu, grad_hidden)
+    grad_pre = torch.empty_like(pre_gelu) if grad_pre is None else grad_pre
+    _same_shape("grad_pre", grad_pre, grad_hidden)
+    st = load_library().act_ffn_gelu_backward(grad_hidden.data_ptr(), pre_gelu.data_ptr(), grad_pre.data_ptr(),
+                                              grad_hidden.numel(), _stream(grad_hidden.device))
+    if st != 0:
+        raise GemmError(st, "act_ffn_gelu_backward")
+    return grad_pre
+
+
+def gelu_inplace(x, pre_gelu=None):
+    """x = gelu(x) in place (tanh approximation); pre_gelu, if given, receives
+    the input values.  Returns x."""
+    _same_shape("x", x, x)
+    if pre_gelu is not None:
+        _same_shape("pre_gelu", pre_gelu, x)
+    st = load_library().act_gelu_inplace(x.data_ptr(), None if pre_gelu is None else pre_gelu.data_ptr(), x.numel(),
+                                         _stream(x.device))
+    if st != 0:
+        raise GemmError(st, "act_gelu_inplace")
+    return x

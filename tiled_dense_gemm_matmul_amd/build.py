@@ -12,6 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gemm_fwd.hip")
 LOSS_SRC = os.path.join(PKG, "csrc", "loss.hip")
+ACT_SRC = os.path.join(PKG, "csrc", "activation.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemmfwd.so")
 PROBE_SRC = os.path.join(PKG, "csrc", "mfma_probe.hip")
@@ -35,8 +36,9 @@ def _hipcc(srcs, lib: str, verbose: bool) -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """The library: the GEMM family (forward and backward) and the fused loss."""
-    return _hipcc([SRC, LOSS_SRC], LIB, verbose)
+    """The library: the GEMM family (forward and backward), the fused loss and
+    the FFN activation kernels."""
+    return _hipcc([SRC, LOSS_SRC, ACT_SRC], LIB, verbose)
 
 
 def build_probe(verbose: bool = False) -> str:

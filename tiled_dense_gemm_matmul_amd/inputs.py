@@ -149,3 +149,12 @@ def loss_case(seed, S, V, *, scale=2.0, ignore_every=0):
     if ignore_every:
         targets[::ignore_every] = V
     return {"logits": logits, "targets": targets}
+
+
+def activation_case(seed, n, *, scale=3.0):
+    """A seeded case for the FFN activation kernels: the hidden gradient g,
+    gate (also used as the GeLU input) and up, n float32 values each; gate is
+    drawn N(0, 1) times `scale` so both tails of the sigmoid and of tanh are
+    exercised."""
+    rng = np.random.default_rng(seed)
+    return {"g": _normal(rng, (n,)), "gate": _normal(rng, (n,)) * np.float32(scale), "up": _normal(rng, (n,))}
