@@ -181,6 +181,41 @@ def time_backward():
         print(json.dumps(row), file=sys.stderr, flush=True)
         lines.append(f"| {label} | {op} [{kcfg}] | {M}×{K}×{N} | {shape_out} | {us:.2f} | {tf:.1f} | "
                      f"{100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f} | {tus:.2f} |")
+    # the FFN down-projection's input gradient followed by the SwiGLU backward:
+    # two launches through HBM (dH written and read back) against the fused one
+    M, K, N = 512, 3072, 768
+    c = inputs.backward_case(7, M, K, N)
+    rng = np.random.default_rng(8)
+    t = {k: torch.from_numpy(v).to(dev) for k, v in c.items()}
+    G = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32) * np.float32(3.0)).to(dev)
+    U = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(dev)
+    dH, dG, dU = (torch.empty((M, K), device=dev) for _ in range(3))
+
+    def two():
+        binding.matmul_t(t["dY"], t["W"], out=dH)
+        binding.ffn_swiglu_backward(dH, G, U, grad_gate=dG, grad_up=dU)
+
+    def fused():
+        binding.matmul_t_swiglu_backward(t["dY"], t["W"], G, U, grad_gate=dG, grad_up=dU)
+
+    res = {}
+    for name, fn in (("separate", two), ("fused", fused)):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(50):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / 50
+    print(json.dumps({"ffn_down_dH_and_swiglu_backward_us": {k: round(v, 2) for k, v in res.items()}}),
+          file=sys.stderr, flush=True)
+    lines += ["", f"FFN down-projection input gradient + SwiGLU backward ({M}×{K}×{N}): matmul_t then "
+                  f"ffn_swiglu_backward {res['separate']:.2f} µs; fused (gemm_matmul_t_swiglu_bwd, dH never "
+                  f"stored) {res['fused']:.2f} µs."]
     print("\n".join(lines))
     return rows
 

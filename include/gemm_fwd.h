@@ -172,6 +172,27 @@ int gemm_matmul_at(const float *X, const float *dY, float *dW, int64_t M, int64_
 int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M, int64_t K,
                             int64_t N, uint32_t flags, void *stream);
 
+/*
+ * Fused SwiGLU backward: dH = dY @ W_down^T (matmul_t of the FFN down-
+ * projection, never stored) turned directly into the gradients of the
+ * SwiGLU inputs, as "ffn_gelu_backward ve ffn_swiglu_backward — FFN
+ * Activation Backward" (sections "Ne Yapar?", "Türevler", "Satır Satır")
+ * defines them on dH:
+ *   dGATE = nan_guard(dH * UP * silu'(GATE)),  dUP = nan_guard(dH * silu(GATE)),
+ *   silu'(x) = s(x) (1 + x (1 - s(x))), s the sign-branched sigmoid, and
+ *   nan_guard mapping NaN and infinities to 0.
+ * dY [M x N], W [K x N] (the down-projection's forward weight, K = d_ff),
+ * GATE, UP, dGATE, dUP [M x K]; fp32, 16-byte aligned.  dGATE and dUP may be
+ * the very arrays GATE or UP (each element is read before it is written) but
+ * may not overlap anything else or each other.  Otherwise as gemm_matmul_t,
+ * without accumulation.  One launch replaces matmul_t plus the element-wise
+ * kernel and never writes or reads dH.
+ */
+int gemm_matmul_t_swiglu_bwd(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                             float *dUP, int64_t M, int64_t K, int64_t N, void *stream);
+int gemm_matmul_t_swiglu_bwd_cfg(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                                 float *dUP, int64_t M, int64_t K, int64_t N, int config, void *stream);
+
 /* The same with an explicit configuration of the backward table (config >= 0,
  * below gemm_bwd_num_configs()), or the library's choice (config < 0). */
 int gemm_matmul_t_cfg(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,

@@ -159,3 +159,80 @@ def test_misaligned_and_flags_are_rejected():
     assert lib.gemm_matmul_t(dY.data_ptr(), W.data_ptr(), out.data_ptr(), 8, 6, 8, 0, st) == -2
     # misaligned pointer
     assert lib.gemm_matmul_at(ctypes.c_void_p(dY.data_ptr() + 4), W.data_ptr(), out.data_ptr(), 8, 8, 8, 0, st) == -3
+
+
+# --- the fused SwiGLU backward: matmul_t's dH turned into dGATE, dUP in the epilogue ---
+
+def fused_ref(case, G, U, rows=None):
+    """The composition of the two pinned oracles, with the bound it implies:
+    dH within the GEMM tolerance, propagated through the element-wise
+    derivatives, plus the element-wise kernels' own tolerance."""
+    from oracle import activation as OA
+    dh, b = oracle.matmul_t(case["dY"], case["W"], rows=rows, want_scale=True)
+    g = G if rows is None else G[rows]
+    u = U if rows is None else U[rows]
+    dg, du, mg, mu = OA.ffn_swiglu_backward(dh, g, u)
+    x = g.astype(np.float64)
+    s = OA.sigmoid(x)
+    dh_err = oracle.TOL_W32[0] * b + oracle.TOL_W32[1]
+    bg = np.abs(u) * s * (1.0 + np.abs(x) * (1.0 - s)) * dh_err + OA.TOL[0] * mg
+    bu = np.abs(x) * s * dh_err + OA.TOL[0] * mu
+    return dg, du, bg, bu
+
+
+def check_fused(y, ref, bound, label):
+    err = np.abs(np.asarray(y, np.float64) - ref)
+    ratio = np.where(bound > 0, err / np.maximum(bound, 1e-300), np.where(err == 0, 0.0, np.inf))
+    fails = int(np.count_nonzero(~(ratio <= 1.0)))
+    say(f"  {label}: max err/tol {float(np.max(ratio)) if ratio.size else 0.0:.3g}, fails {fails} of {ratio.size}")
+    assert fails == 0
+
+
+def fused_case(seed, M, K, N):
+    c = inputs.backward_case(seed, M, K, N)
+    rng = np.random.default_rng(seed + 1)
+    G = (rng.standard_normal((M, K), dtype=np.float32) * np.float32(3.0))
+    U = rng.standard_normal((M, K), dtype=np.float32)
+    return c, G, U
+
+
+@pytest.mark.parametrize("M,K,N", [(77, 132, 100), (130, 68, 196), (33, 260, 52), (512, 3072, 768)])
+def test_fused_swiglu_backward(M, K, N):
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    say(f"fused swiglu backward M={M} K={K} N={N}")
+    c, G, U = fused_case(M * 3 + K, M, K, N)
+    dg, du = binding.matmul_t_swiglu_backward(to_dev(c["dY"]), to_dev(c["W"]), to_dev(G), to_dev(U))
+    torch.cuda.synchronize()
+    rows = None if M * K < 1e6 else np.unique(np.concatenate([[0, M - 1], np.random.default_rng(1).choice(M, 30)]))
+    rg, ru, bg, bu = fused_ref(c, G, U, rows=rows)
+    sel = slice(None) if rows is None else rows
+    check_fused(dg.cpu().numpy()[sel], rg, bg, "dGATE")
+    check_fused(du.cpu().numpy()[sel], ru, bu, "dUP")
+
+
+def test_fused_swiglu_backward_every_config_and_in_place():
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    M, K, N = 130, 68, 196
+    c, G, U = fused_case(5, M, K, N)
+    rg, ru, bg, bu = fused_ref(c, G, U)
+    for cfg in range(binding.bwd_num_configs()):
+        say(f"fused swiglu backward config {binding.bwd_config_name(cfg)}")
+        dg, du = binding.matmul_t_swiglu_backward(to_dev(c["dY"]), to_dev(c["W"]), to_dev(G), to_dev(U), config=cfg)
+        torch.cuda.synchronize()
+        check_fused(dg.cpu().numpy(), rg, bg, f"dGATE {binding.bwd_config_name(cfg)}")
+        check_fused(du.cpu().numpy(), ru, bu, f"dUP {binding.bwd_config_name(cfg)}")
+    # the gradients written over GATE and UP themselves
+    g, u = to_dev(G), to_dev(U)
+    binding.matmul_t_swiglu_backward(to_dev(c["dY"]), to_dev(c["W"]), g, u, grad_gate=g, grad_up=u)
+    torch.cuda.synchronize()
+    check_fused(g.cpu().numpy(), rg, bg, "dGATE over GATE")
+    check_fused(u.cpu().numpy(), ru, bu, "dUP over UP")
+    # empty contraction: dH = 0, both gradients zero
+    dev = device()
+    z = torch.empty((6, 0), device=dev)
+    dg, du = binding.matmul_t_swiglu_backward(z, torch.empty((8, 0), device=dev), torch.randn((6, 8), device=dev),
+                                              torch.randn((6, 8), device=dev))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dg).item() == 0 and torch.count_nonzero(du).item() == 0

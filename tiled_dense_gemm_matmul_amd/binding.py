@@ -25,7 +25,7 @@ EXPORTED = (
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
     "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
     "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
-    "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward", "act_gelu_inplace",
+    "gemm_matmul_t_swiglu_bwd", "gemm_matmul_t_swiglu_bwd_cfg", "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward", "act_gelu_inplace",
 )
 
 
@@ -74,6 +74,10 @@ def load_library():
         getattr(lib, name).restype = c_int
         getattr(lib, name + "_cfg").argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, c_int, p]
         getattr(lib, name + "_cfg").restype = c_int
+    lib.gemm_matmul_t_swiglu_bwd.argtypes = [p] * 6 + [i64, i64, i64, p]
+    lib.gemm_matmul_t_swiglu_bwd.restype = c_int
+    lib.gemm_matmul_t_swiglu_bwd_cfg.argtypes = [p] * 6 + [i64, i64, i64, c_int, p]
+    lib.gemm_matmul_t_swiglu_bwd_cfg.restype = c_int
     lib.gemm_bwd_num_configs.argtypes = []
     lib.gemm_bwd_num_configs.restype = c_int
     lib.gemm_bwd_config_name.argtypes = [c_int]
@@ -303,6 +307,38 @@ def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None):
     _bwd_call("gemm_matmul_at_swiglu_a", (G.data_ptr(), U.data_ptr(), dY.data_ptr(), out.data_ptr()),
               M, K, N, acc, device, config)
     return out
+
+
+def matmul_t_swiglu_backward(dY, W, G, U, grad_gate=None, grad_up=None, config=None):
+    """The FFN down-projection's input gradient dH = dY @ W^T turned straight
+    into the SwiGLU gradients (dH itself is never stored):
+    grad_gate = nan_guard(dH * U * silu'(G)), grad_up = nan_guard(dH * silu(G)).
+    dY [M, N], W [K, N] (the forward weight), G, U [M, K] f32.
+    Returns (grad_gate, grad_up); either may be given as G or U to overwrite it."""
+    if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+        raise TypeError("dY must be a 2-D torch.Tensor [M, N]")
+    M, N = dY.shape
+    device = dY.device
+    _check_act(dY, "dY", (M, N), device)
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise TypeError("W must be a 2-D torch.Tensor [K, N]")
+    K = W.shape[0]
+    _check_act(W, "W", (K, N), device)
+    _check_act(G, "G", (M, K), device)
+    _check_act(U, "U", (M, K), device)
+    grad_gate = torch.empty((M, K), dtype=torch.float32, device=device) if grad_gate is None else grad_gate
+    grad_up = torch.empty((M, K), dtype=torch.float32, device=device) if grad_up is None else grad_up
+    _check_act(grad_gate, "grad_gate", (M, K), device)
+    _check_act(grad_up, "grad_up", (M, K), device)
+    lib = load_library()
+    ptrs = (dY.data_ptr(), W.data_ptr(), G.data_ptr(), U.data_ptr(), grad_gate.data_ptr(), grad_up.data_ptr())
+    if config is None or config < 0:
+        st = lib.gemm_matmul_t_swiglu_bwd(*ptrs, M, K, N, _stream(device))
+    else:
+        st = lib.gemm_matmul_t_swiglu_bwd_cfg(*ptrs, M, K, N, int(config), _stream(device))
+    if st != 0:
+        raise GemmError(st, "gemm_matmul_t_swiglu_bwd")
+    return grad_gate, grad_up
 
 
 # --- fused loss (include/loss.h) ---

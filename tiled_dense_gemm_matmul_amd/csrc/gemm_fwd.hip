@@ -60,6 +60,10 @@ struct Params {
     const void *W;
     const float *R;
     float *Y;
+    // fused SwiGLU backward epilogue only: GATE and UP [M x N] in, d UP out
+    // (d GATE goes to Y)
+    const float *EG, *EU;
+    float *Y2;
     int M, K, N;
     int tiles_m, tiles_n;
     int group_m;     // M-tiles per group in the tile order
@@ -239,7 +243,29 @@ struct StageRegs {
 // reads per fragment), whichever its memory layout makes a plain copy.
 constexpr int kOpNN = 0, kOpNT = 1, kOpTN = 2;
 
-template <class C, bool SWIGLU, bool W16, bool RESID, int OP = kOpNN>
+// Epilogues.  kEpiStore: Y = acc (+ R).  kEpiSwigluBwd: acc is the gradient
+// dH of the SwiGLU activation H = silu(GATE) * UP, which is not stored;
+// instead Y = dGATE = nan_guard(dH UP silu'(GATE)) and Y2 = dUP =
+// nan_guard(dH silu(GATE)), with silu'(x) = s (1 + x (1 - s)), s the
+// sign-branched sigmoid ("ffn_gelu_backward ve ffn_swiglu_backward",
+// sections "Türevler" and "Satır Satır").
+constexpr int kEpiStore = 0, kEpiSwigluBwd = 1;
+
+__device__ __forceinline__ float nan_guard(float x) { return __builtin_isfinite(x) ? x : 0.0f; }
+
+__device__ __forceinline__ void swiglu_bwd4(f32x4 dh, f32x4 g, f32x4 u, f32x4 &dg, f32x4 &du) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float x = g[c];
+        const float e = __expf(-__builtin_fabsf(x));
+        const float r = 1.0f / (1.0f + e);
+        const float sg = x >= 0.0f ? r : e * r;
+        dg[c] = nan_guard(dh[c] * u[c] * (sg * (1.0f + x * (1.0f - sg))));
+        du[c] = nan_guard(dh[c] * (x * sg));
+    }
+}
+
+template <class C, bool SWIGLU, bool W16, bool RESID, int OP = kOpNN, int EPI = kEpiStore>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK;
     constexpr int WM = C::WM, WN = C::WN, WK = C::WK;
@@ -759,6 +785,27 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     __syncthreads();
 
     const size_t tile_off = (size_t)m0 * N + n0;
+    // The last step of the epilogue for four consecutive outputs at byte
+    // offset `off` of the tile (kOOB for masked items): store them (plus R),
+    // or turn them into the two SwiGLU gradients.
+    auto make_finish = [&](int ybytes) {
+        const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
+        const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
+        const Rsrc rG = EPI == kEpiSwigluBwd ? make_rsrc(p.EG + tile_off, ybytes) : rY;
+        const Rsrc rU = EPI == kEpiSwigluBwd ? make_rsrc(p.EU + tile_off, ybytes) : rY;
+        const Rsrc rY2 = EPI == kEpiSwigluBwd ? make_rsrc(p.Y2 + tile_off, ybytes) : rY;
+        return [=](f32x4 v, int off) {
+            if constexpr (EPI == kEpiSwigluBwd) {
+                f32x4 dg, du;
+                swiglu_bwd4(v, load_f32x4(rG, off), load_f32x4(rU, off), dg, du);
+                store_f32x4(rY, off, dg);
+                store_f32x4(rY2, off, du);
+            } else {
+                if constexpr (RESID) v += load_f32x4(rR, off);
+                store_f32x4(rY, off, v);
+            }
+        };
+    };
     constexpr int Q = BN / 4;
     constexpr int ITEMS = BM * Q;
     if constexpr (KS > 1) {
@@ -797,8 +844,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         if (tid == 0)
             __hip_atomic_store(&g_sk_cnt[p.region][tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int ybytes = rows_valid * N * 4;
-        const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
-        const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
+        const auto finish = make_finish(ybytes);
 #pragma unroll
         for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
             const int idx = tid + it * NC;
@@ -823,8 +869,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     v += load_f32x4_coherent(rP, off);
                 }
             }
-            if constexpr (RESID) v += load_f32x4(rR, off);
-            store_f32x4(rY, off, v);
+            finish(v, off);
         }
         return;
     }
@@ -833,8 +878,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     // The tile's valid rows span rows_valid * N elements from its origin
     // (under 2^30 bytes by the shape limits); masked items use kOOB.
     const int ybytes = rows_valid * N * 4;
-    const Rsrc rY = make_rsrc(p.Y + tile_off, ybytes);
-    const Rsrc rR = RESID ? make_rsrc(p.R + tile_off, ybytes) : rY;
+    const auto finish = make_finish(ybytes);
 #pragma unroll
     for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
         const int idx = tid + it * NC;
@@ -846,8 +890,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             v += *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * CSTR + c4 * 4);
         const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
         const int off = ok ? (row * N + c4 * 4) * 4 : kOOB;
-        if constexpr (RESID) v += load_f32x4(rR, off);
-        store_f32x4(rY, off, v);
+        finish(v, off);
     }
 }
 
@@ -934,12 +977,14 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 // The backward products use the configurations that the forward selection
 // picks from, under the same names: fn[op == kOpTN][swiglu][accumulate].
-// matmul_t (kOpNT) has no SwiGLU form.
+// For matmul_t (kOpNT) the SwiGLU slot holds the fused SwiGLU backward
+// (matmul_t's product dH turned into dGATE and dUP in the epilogue), which
+// has no accumulating form.
 template <class C>
 constexpr ConfigEntry make_bwd_entry(const char *name) {
     return ConfigEntry{name, C::BM, C::BN, C::BK, C::NT, C::KS,
                        {{{gemm_fwd_kernel<C, false, false, false, kOpNT>, gemm_fwd_kernel<C, false, false, true, kOpNT>},
-                         {nullptr, nullptr}},
+                         {gemm_fwd_kernel<C, false, false, false, kOpNT, kEpiSwigluBwd>, nullptr}},
                         {{gemm_fwd_kernel<C, false, false, false, kOpTN>, gemm_fwd_kernel<C, false, false, true, kOpTN>},
                          {gemm_fwd_kernel<C, true, false, false, kOpTN>, gemm_fwd_kernel<C, true, false, true, kOpTN>}}}};
 }
@@ -1082,6 +1127,7 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     if (e.ks > 1 && !split_fits(e, M, N)) return GEMM_ERR_CONFIG;
     Params p;
     p.A = A; p.U = U; p.W = W; p.R = R; p.Y = Y;
+    p.EG = nullptr; p.EU = nullptr; p.Y2 = nullptr;
     p.M = (int)M; p.K = (int)K; p.N = (int)N;
     p.tiles_m = (int)ceil_div(M, e.bm);
     p.tiles_n = (int)ceil_div(N, e.bn);
@@ -1105,40 +1151,63 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
 // with A = X, or silu(GATE) * UP.  `acc` adds the product to the output's
 // current contents.
 int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B, float *Y, int64_t M,
-            int64_t K, int64_t N, bool acc, int config, void *stream) {
+            int64_t K, int64_t N, bool acc, int config, void *stream, const float *EG = nullptr,
+            const float *EU = nullptr, float *Y2 = nullptr) {
+    // op kOpNT with swiglu: the fused SwiGLU backward, dGATE into Y and dUP
+    // into Y2 from GATE (EG) and UP (EU), all [M x K]
+    const bool fused = op == kOpNT && swiglu;
     const int64_t lim = (int64_t)1 << 31;
     if (M < 0 || K < 0 || N < 0 || M >= lim || K >= lim || N >= lim) return GEMM_ERR_SHAPE;
     const bool mk = M > 0 && K > 0, kn = K > 0 && N > 0, mn = M > 0 && N > 0;
     const bool a_null = op == kOpNT ? (mn && A == nullptr) : (mk && (A == nullptr || (swiglu && U == nullptr)));
     const bool b_null = op == kOpNT ? (kn && B == nullptr) : (mn && B == nullptr);
     const bool y_null = op == kOpNT ? (mk && Y == nullptr) : (kn && Y == nullptr);
-    if (a_null || b_null || y_null) return GEMM_ERR_NULL;
+    const bool e_null = fused && mk && (EG == nullptr || EU == nullptr || Y2 == nullptr);
+    if (a_null || b_null || y_null || e_null) return GEMM_ERR_NULL;
+    if (fused && acc) return GEMM_ERR_DTYPE;
     if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
     if (K * 1024 >= lim || N * 1024 >= lim) return GEMM_ERR_SHAPE;
     if (config >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
-    if ((A && !aligned(A, 16)) || (U && !aligned(U, 16)) || (B && !aligned(B, 16)) || (Y && !aligned(Y, 16)))
+    if ((A && !aligned(A, 16)) || (U && !aligned(U, 16)) || (B && !aligned(B, 16)) || (Y && !aligned(Y, 16)) ||
+        (EG && !aligned(EG, 16)) || (EU && !aligned(EU, 16)) || (Y2 && !aligned(Y2, 16)))
         return GEMM_ERR_ALIGN;
     const size_t abytes = (size_t)(op == kOpNT ? M * N : M * K) * 4;
     const size_t bbytes = (size_t)(op == kOpNT ? K * N : M * N) * 4;
     const size_t ybytes = (size_t)(op == kOpNT ? M * K : K * N) * 4;
     if (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, U, abytes) || overlaps(Y, ybytes, B, bbytes))
         return GEMM_ERR_ALIAS;
+    if (fused) {
+        // each output may be GATE's or UP's very array (every element is read
+        // before it is written, by one thread) but overlaps nothing else
+        auto partial = [&](const void *o, const void *i) { return o != i && overlaps(o, ybytes, i, ybytes); };
+        if (overlaps(Y2, ybytes, A, abytes) || overlaps(Y2, ybytes, B, bbytes) || overlaps(Y, ybytes, Y2, ybytes) ||
+            partial(Y, EG) || partial(Y, EU) || partial(Y2, EG) || partial(Y2, EU))
+            return GEMM_ERR_ALIAS;
+    }
     // kernel dimensions: output rows, contraction, output columns
     const int64_t km = op == kOpNT ? M : K, kk = op == kOpNT ? N : M, kn2 = op == kOpNT ? K : N;
     if (km == 0 || kn2 == 0) return GEMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kk == 0 && fused) {
+        // dH = 0: both gradients are zero
+        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, nullptr, Y, km * kn2);
+        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, nullptr, Y2,
+                           km * kn2);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
     if (kk == 0) {
         if (acc) return GEMM_OK;  // nothing to add
         const int64_t count = km * kn2;
         hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, nullptr, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
-    const int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, swiglu);
+    const int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu);
     if (cfg < 0 || cfg >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
     const ConfigEntry &e = kBwdConfigs[cfg];
     if (e.ks > 1 && !split_fits(e, km, kn2)) return GEMM_ERR_CONFIG;
     Params p;
     p.A = A; p.U = U; p.W = B; p.R = acc ? Y : nullptr; p.Y = Y;
+    p.EG = EG; p.EU = EU; p.Y2 = Y2;
     p.M = (int)km; p.K = (int)kk; p.N = (int)kn2;
     p.tiles_m = (int)ceil_div(km, e.bm);
     p.tiles_n = (int)ceil_div(kn2, e.bn);
@@ -1217,6 +1286,15 @@ int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float 
 int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M, int64_t K,
                             int64_t N, uint32_t flags, void *stream) {
     return gemm_matmul_at_swiglu_a_cfg(GATE, UP, dY, dW, M, K, N, flags, -1, stream);
+}
+
+int gemm_matmul_t_swiglu_bwd_cfg(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                                 float *dUP, int64_t M, int64_t K, int64_t N, int config, void *stream) {
+    return run_bwd(kOpNT, true, dY, nullptr, W, dGATE, M, K, N, false, config, stream, GATE, UP, dUP);
+}
+int gemm_matmul_t_swiglu_bwd(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                             float *dUP, int64_t M, int64_t K, int64_t N, void *stream) {
+    return gemm_matmul_t_swiglu_bwd_cfg(dY, W, GATE, UP, dGATE, dUP, M, K, N, -1, stream);
 }
 
 int gemm_bwd_num_configs(void) { return kNumBwdConfigs; }
