@@ -423,14 +423,15 @@ def counters_from(base):
     lines = [
         "# Hardware counters of the seq-512 forward step (bench.py)",
         "",
-        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host), one counter set per run:",
+        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host and $OUT an output "
+        "directory), one counter set per run:",
         "",
     ]
     for run, ctrs in COUNTER_PASSES.items():
-        lines.append(f"    rocprofv3 --pmc {ctrs} -f csv -d $R/gpurun_out/counters/{run} -o pmc -- "
+        lines.append(f"    rocprofv3 --pmc {ctrs} -f csv -d $OUT/counters/{run} -o pmc -- "
                      "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu")
     lines += [
-        "    python3 bench.py --counters-from gpurun_out/counters      # writes this file",
+        "    python3 bench.py --counters-from $OUT/counters      # writes this file",
         "",
         "Averages over every launch of each kernel in those runs.  Counter collection serialises launches and",
         "slows the kernels (the `µs under counters` column), so the busy fractions are lower than in an",
@@ -730,8 +731,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the GEMM shards by rows or columns with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the kernels have no multi-GPU path "
+              "(the GEMMs shard by rows or by columns with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
