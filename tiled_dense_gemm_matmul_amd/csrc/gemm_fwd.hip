@@ -998,6 +998,8 @@ const ConfigEntry kBwdConfigs[] = {
     make_bwd_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
     make_bwd_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
     make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    // long contractions on small outputs (the lm_head's dX: 512 x 16384 x 768)
+    make_bwd_entry<Tile<128, 96, 64, 2, 2, 1, 8, 3, 1, 1, 8, 1, 2, 1>>("128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"),
 };
 constexpr int kNumBwdConfigs = sizeof(kBwdConfigs) / sizeof(kBwdConfigs[0]);
 
@@ -1061,16 +1063,23 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
 // tiles lose to 32 x 48 tiles with the K range split over four waves (about
 // 20% at 768 x 512 x 3072 and 3072 x 512 x 768).  With a transposed B and a
 // contraction of a few thousand, 16 x 48 tiles with BK = 128 beat the
-// two-workgroup split-K (6% at 512 x 3072 x 768); at 16384 the split wins.
+// two-workgroup split-K (6% at 512 x 3072 x 768).  With a contraction of
+// 8192 or more, 128 x 96 tiles with the K range split eight ways re-read the
+// transposed B a quarter as often as 32 x 96 tiles and win by 12% (the
+// lm_head's dX, 512 x 16384 x 768).
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4");
     static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
     static const int tiny = table_index(kBwdConfigs, kNumBwdConfigs, "16x48x128_k4_sp4_dAW");
+    static const int long_k = table_index(kBwdConfigs, kNumBwdConfigs, "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
     const int f = select_config(M, K, N, swiglu, 0);
     if (f < 0) return -1;
     if (op == kOpTN && f == fwd_mid) return small;
     if (op == kOpNT && f == fwd_deep_split && K <= 4096) return tiny;
+    if (op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
+        ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
+        return long_k;
     return table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
 }
 
