@@ -1,8 +1,12 @@
-// Forward linear-layer GEMM family for MI355X (gfx950): HIP kernels + C ABI.
+// Linear-layer GEMM family for MI355X (gfx950): HIP kernels + C ABI.
 //
 // Operations ("matmul ve matmul_residual — Tiled Matrix Multiply (Forward)",
 // https://llm.istanbul/learn/tr/03_linear_forward, section "Ne Yapar?"):
-//   Y = A @ W (+ R),  A = X  or  A = silu(GATE) * UP,  W fp32 or binary16.
+//   Y = A @ W (+ R),  A = X  or  A = silu(GATE) * UP,  W fp32 or binary16,
+// and the backward kernels the same section names: dX = dY @ W^T
+// (matmul_t), dW = A^T @ dY (matmul_at, A recomputed as silu(GATE) * UP for
+// _swiglu_a), each optionally accumulating into the output (_acc), plus
+// matmul_t with the SwiGLU backward fused into its epilogue.
 //
 // Design (gfx950, wave64, fp32 matrix cores):
 //  * One workgroup owns one BM x BN output tile over its K range (the page's
@@ -38,6 +42,9 @@
 //    tiles and its private L2 sees reuse of both operands.
 //  * Edges: rows >= M, columns >= N and k >= K are staged as zeros and never
 //    read; stores are masked to i < M, j < N.
+//  * The backward products give one operand transposed; it is staged in the
+//    other operand's LDS layout (see the operand layouts below), so one
+//    kernel template serves all of them.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
