@@ -96,11 +96,17 @@ __device__ unsigned g_sk_cnt[kSkRegions][kSkMaxTiles];
 // device helpers
 // ---------------------------------------------------------------------------
 
-// Slot permutation of a K-major LDS row: float4 slot s of row r lives at
-// s ^ swz(r).  For 8 consecutive rows, and for 8 rows spaced 4 apart, the
-// values are all distinct, which keeps both the fragment reads (consecutive
-// rows) and the transposed W writes (rows 4 apart) on distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
+// Slot permutation of a K-major LDS row of SL float4 slots: slot s of row r
+// lives at s ^ swz<SL>(r).  A 16-byte fragment read serves 16 lanes (16
+// consecutive rows, one slot each) per LDS cycle over the 64 banks, so the
+// 16 rows must land on 16 distinct 4-bank groups.  With 8-slot rows (32
+// banks) consecutive rows alternate bank halves and 8 distinct values per 8
+// rows suffice; with 16 or more slots every row starts on bank 0 and the
+// permutation needs 4 bits: r ^ (r >> 2) is a bijection on each aligned
+// block of 16 rows.  (A 3-bit permutation there measured two LDS cycles per
+// read instead of one.)
+template <int SL>
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & (SL >= 16 ? 15 : 7); }
 
 // silu(g) * u = g * u / (1 + exp(-g)), the sigmoid of "ffn_gelu_backward ve
 // ffn_swiglu_backward — FFN Activation Backward" ("Türevler / SiLU'").  The
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < A_DIT; ++j) {
         const int q = (pw + j * NPW) * 64 + lane;
-        const int row = q / SL, logical = (q % SL) ^ swz(row);
+        const int row = q / SL, logical = (q % SL) ^ swz<SL>(row);
         ad_gk[j] = logical * 4;
         ad_off[j] = (row * K + logical * 4) * 4;
     }
@@ -519,7 +525,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 *reinterpret_cast<f32x4 *>(As + k * ASTR + mq * 4) = v;
             } else {
                 const int row = f / SL, slot = f % SL;
-                *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4) = v;
+                *reinterpret_cast<f32x4 *>(As + (row * SL + (slot ^ swz<SL>(row))) * 4) = v;
             }
         }
 #pragma unroll
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             if (B_IT * NS != B_ITEMS && mb >= B_ITEMS) continue;
             if constexpr (BT) {
                 const int row = mb / SL, slot = mb % SL;
-                *reinterpret_cast<f32x4 *>(Bs + (row * SL + (slot ^ swz(row))) * 4) = r.b[i];
+                *reinterpret_cast<f32x4 *>(Bs + (row * SL + (slot ^ swz<SL>(row))) * 4) = r.b[i];
                 continue;
             }
             const int k = mb / NQ, nq = mb % NQ;
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     af[i] = f32x4{a[0], a[ASTR], a[2 * ASTR], a[3 * ASTR]};
                 } else {
                     const int row = wm * WTM + i * 16 + r16;
-                    af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz(row))) * 4);
+                    af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz<SL>(row))) * 4);
                 }
             }
             // W is N-major in LDS: the four k of a lane are four rows; the row
@@ -573,7 +579,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             for (int j = 0; j < TN; ++j) {
                 if constexpr (BT) {
                     const int row = wn * WTN + j * 16 + r16;
-                    bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (row * SL + (slot ^ swz(row))) * 4);
+                    bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (row * SL + (slot ^ swz<SL>(row))) * 4);
                 } else {
                     const float *b = Bs + (c * 16 + q4 * 4) * BSTR + wn * WTN + j * 16 + r16;
                     bf[j] = f32x4{b[0], b[BSTR], b[2 * BSTR], b[3 * BSTR]};
