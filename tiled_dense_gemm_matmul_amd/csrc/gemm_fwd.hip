@@ -97,16 +97,30 @@ __device__ unsigned g_sk_cnt[kSkRegions][kSkMaxTiles];
 // ---------------------------------------------------------------------------
 
 // Slot permutation of a K-major LDS row of SL float4 slots: slot s of row r
-// lives at s ^ swz<SL>(r).  A 16-byte fragment read serves 16 lanes (16
-// consecutive rows, one slot each) per LDS cycle over the 64 banks, so the
-// 16 rows must land on 16 distinct 4-bank groups.  With 8-slot rows (32
-// banks) consecutive rows alternate bank halves and 8 distinct values per 8
-// rows suffice; with 16 or more slots every row starts on bank 0 and the
-// permutation needs 4 bits: r ^ (r >> 2) is a bijection on each aligned
-// block of 16 rows.  (A 3-bit permutation there measured two LDS cycles per
-// read instead of one.)
+// lives at s ^ swz<SL>(r).  A 16-byte fragment read covers 16 consecutive
+// rows at one logical slot; measured with the bank-conflict counter, it takes
+// the minimum 4 LDS cycles with the permutations below.
+//  - 8-slot rows (128 bytes, so consecutive rows alternate between the two
+//    halves of the 64 banks): r ^ (r >> 2) in 3 bits.
+//  - 16 or more slots (every row starts on bank 0): the permutation must
+//    spread 16 rows over 16 slots, so it takes 4 bits; the 3-bit one took
+//    8 cycles per read here.  r ^ (r >> 2) in 4 bits is a bijection on each
+//    aligned block of 16 rows.  For 32-slot rows it is taken of r mod 16, so
+//    that it repeats every 16 rows and the fragments of one wave (rows 16
+//    apart) share one address: with three fragments per wave that saved 6%
+//    of a 16 x 48 x 128 kernel's time, while on 16-slot rows the full-row
+//    form measured 1% faster.
 template <int SL>
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & (SL >= 16 ? 15 : 7); }
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (SL >= 32) {
+        const int b = r & 15;
+        return b ^ (b >> 2);
+    } else if constexpr (SL == 16) {
+        return (r ^ (r >> 2)) & 15;
+    } else {
+        return (r ^ (r >> 2)) & 7;
+    }
+}
 
 // silu(g) * u = g * u / (1 + exp(-g)), the sigmoid of "ffn_gelu_backward ve
 // ffn_swiglu_backward — FFN Activation Backward" ("Türevler / SiLU'").  The
