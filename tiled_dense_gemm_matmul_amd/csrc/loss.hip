@@ -19,6 +19,9 @@
 //    partials in a fixed order from LDS.  Each reduction has its own LDS
 //    slots, so consecutive reductions need no trailing barrier.
 //  * exp(l - max) is computed once per element and kept for the gradient.
+//  * Logit arrays of 256 MiB or more (past the Infinity Cache) are read and
+//    written with the non-temporal cache policy; smaller ones, which the cache
+//    can hold, keep the default.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -35,6 +38,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((vector_size(16)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kOOB = (int)0x80000000u;
+constexpr int kNonTemporal = 2;                       // buffer-access cache policy: nt
+constexpr int64_t kStreamBytes = (int64_t)256 << 20;  // arrays past the Infinity Cache
 
 __device__ __forceinline__ Rsrc row_rsrc(const void *base, int bytes) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -80,12 +85,13 @@ __device__ __forceinline__ float row_loss(float lse, float l_t, float mean_l, fl
 // is fetched and stored at an offset past the buffer's range, so its loads
 // return zeros and its stores are dropped, and it is left out of the
 // reductions by comparing j with the thread's count of valid groups.
-template <int NT, int CAP, bool VEC>
+template <int NT, int CAP, bool VEC, bool STREAM>
 __global__ __launch_bounds__(NT) void cross_entropy_resident(float *logits, const uint32_t *tgts, float *losses,
                                                              int V, float alpha, float beta, float inv_norm) {
     constexpr int NW = NT / 64;
     constexpr int W = VEC ? 4 : 1;
     constexpr int G = CAP / W;
+    constexpr int POL = STREAM ? kNonTemporal : 0;  // cache policy of the row's loads and stores
     __shared__ float red[3][NW];
     const int tid = threadIdx.x;
     const int s = blockIdx.x;
@@ -98,8 +104,8 @@ __global__ __launch_bounds__(NT) void cross_entropy_resident(float *logits, cons
         if (tid == 0) losses[s] = 0.0f;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            if (VEC) __builtin_amdgcn_raw_buffer_store_b128(u32x4v{0u, 0u, 0u, 0u}, rr, off(j), 0, 0);
-            else __builtin_amdgcn_raw_buffer_store_b32(0u, rr, off(j), 0, 0);
+            if (VEC) __builtin_amdgcn_raw_buffer_store_b128(u32x4v{0u, 0u, 0u, 0u}, rr, off(j), 0, POL);
+            else __builtin_amdgcn_raw_buffer_store_b32(0u, rr, off(j), 0, POL);
         }
         return;
     }
@@ -109,10 +115,10 @@ __global__ __launch_bounds__(NT) void cross_entropy_resident(float *logits, cons
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         if (VEC) {
-            const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off(j), 0, 0));
+            const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off(j), 0, POL));
             x[4 * j] = q.x; x[4 * j + 1] = q.y; x[4 * j + 2] = q.z; x[4 * j + 3] = q.w;
         } else {
-            x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, off(j), 0, 0));
+            x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, off(j), 0, POL));
         }
     }
     // phase 1: row max (and the plain sum for label smoothing)
@@ -169,9 +175,9 @@ __global__ __launch_bounds__(NT) void cross_entropy_resident(float *logits, cons
         }
         if (VEC) {
             const f32x4 q = f32x4{g[0], g[W > 1 ? 1 : 0], g[W > 2 ? 2 : 0], g[W > 3 ? 3 : 0]};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, q), rr, off(j), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, q), rr, off(j), 0, POL);
         } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, g[0]), rr, off(j), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, g[0]), rr, off(j), 0, POL);
         }
     }
 }
@@ -252,11 +258,14 @@ int loss_cross_entropy(float *logits, const uint32_t *targets, float *losses, in
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int s = (int)S, v = (int)V;
     const bool vec = V % 4 == 0 && aligned(logits, 16);
+    const bool stream_hint = S * V * 4 >= kStreamBytes;
     if (V <= 256 * 64) {
-        if (vec) hipLaunchKernelGGL((cross_entropy_resident<256, 64, true>), dim3(s), dim3(256), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
-        else hipLaunchKernelGGL((cross_entropy_resident<256, 64, false>), dim3(s), dim3(256), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
+        if (vec && stream_hint) hipLaunchKernelGGL((cross_entropy_resident<256, 64, true, true>), dim3(s), dim3(256), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
+        else if (vec) hipLaunchKernelGGL((cross_entropy_resident<256, 64, true, false>), dim3(s), dim3(256), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
+        else hipLaunchKernelGGL((cross_entropy_resident<256, 64, false, false>), dim3(s), dim3(256), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
     } else if (V <= 1024 * 64 && vec) {
-        hipLaunchKernelGGL((cross_entropy_resident<1024, 64, true>), dim3(s), dim3(1024), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
+        if (stream_hint) hipLaunchKernelGGL((cross_entropy_resident<1024, 64, true, true>), dim3(s), dim3(1024), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
+        else hipLaunchKernelGGL((cross_entropy_resident<1024, 64, true, false>), dim3(s), dim3(1024), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
     } else {
         hipLaunchKernelGGL((cross_entropy_stream<1024>), dim3(s), dim3(1024), 0, st, logits, targets, losses, v, alpha, beta, inv_norm);
     }
