@@ -204,6 +204,15 @@ def test_backward_selection(lib):
     assert lib.gemm_bwd_select_config(0, 512, 768, 768, 0) == -1
     assert lib.gemm_bwd_select_config(3, 512, 768, 768, 0) == -1
 
+    def name(op, *shape):
+        return lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(op, *shape, 0)).decode()
+    # dW of the 768 x 768 projections: 384 tiles of 32 x 48 would take two
+    # rounds on 256 CUs, 256 tiles of 48 x 48 take one
+    assert name(2, 512, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 512, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 512, 3072, 768) == "32x48x64_k4_sp4_pf3_dAW"
+    assert name(1, 512, 768, 16384) == "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"
+
 
 def test_loss_exports_and_validation(lib):
     """include/loss.h: every declared function is exported, and bad arguments

@@ -1028,6 +1028,9 @@ const ConfigEntry kBwdConfigs[] = {
     make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
     // long contractions on small outputs (the lm_head's dX: 512 x 16384 x 768)
     make_bwd_entry<Tile<128, 96, 64, 2, 2, 1, 8, 3, 1, 1, 8, 1, 2, 1>>("128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"),
+    // transposed A whose 32 x 48 grid would leave half the CUs a second
+    // tile (the attention projections' dW, 768 x 512 x 768)
+    make_bwd_entry<Tile<48, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("48x48x64_k4_sp4_pf3_dAW"),
 };
 constexpr int kNumBwdConfigs = sizeof(kBwdConfigs) / sizeof(kBwdConfigs[0]);
 
@@ -1099,13 +1102,18 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
 // two-workgroup split-K (6% at 512 x 3072 x 768).  With a contraction of
 // 8192 or more, 128 x 96 tiles with the K range split eight ways re-read the
 // transposed B a quarter as often as 32 x 96 tiles and win by 12% (the
-// lm_head's dX, 512 x 16384 x 768).
+// lm_head's dX, 512 x 16384 x 768).  And where those 32 x 48 tiles of a
+// transposed A come to between one and two per CU while 48 x 48 tiles come
+// to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
+// at 768 x 512 x 768.
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4");
     static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
     static const int tiny = table_index(kBwdConfigs, kNumBwdConfigs, "16x48x128_k4_sp4_dAW");
     static const int long_k = table_index(kBwdConfigs, kNumBwdConfigs, "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
+    static const int square = table_index(kBwdConfigs, kNumBwdConfigs, "48x48x64_k4_sp4_pf3_dAW");
+    const int64_t cus = 256;
     // the forward rule without its SwiGLU tile, which the backward table
     // does not hold
     (void)swiglu;
@@ -1116,7 +1124,12 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
     if (op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
         return long_k;
-    return table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    const int r = table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    if (op == kOpTN && r == small) {
+        const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
+        if (t32 > cus && t32 < 2 * cus && t48 <= cus) return square;
+    }
+    return r;
 }
 
 // ---------------------------------------------------------------------------
