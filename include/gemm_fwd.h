@@ -40,16 +40,23 @@
  * the library may split K over several workgroups per output tile; their
  * fp32 partial tiles meet in a static device workspace that the library
  * holds for the life of the process (64 MiB plus 64 KiB of counters per
- * device), so no call allocates.  Successive calls rotate over 4 regions of
- * it: at most 4 such calls may be in flight at once on one device (calls on
- * one stream never overlap; more than 4 streams running split-K calls
- * concurrently would race).  The counters are left at zero by every call.
+ * device), so no call allocates.  The workspace has 4 regions, and each
+ * belongs to one stream: the first 4 distinct streams (by handle) that make
+ * a split-K call each keep a region for the life of the process, and calls
+ * on one stream, which run in order, share it.  Calls on a later stream get
+ * no region: the library's own tile choice then takes a configuration
+ * without split-K (same results within the tolerance, not bit for bit), and
+ * an explicit split-K configuration gives GEMM_ERR_CONFIG.  So split-K calls
+ * on different streams never share workspace.  The special per-thread
+ * default stream handle counts as a single stream: callers that use it from
+ * several host threads at once must not rely on split-K configurations.  The
+ * counters are left at zero by every call.
  *
  * Errors.  Arguments are validated synchronously before anything is enqueued;
  * on a negative status nothing is launched and Y is untouched.  No exception or
  * abort crosses this interface.  Calls may be made from several host threads;
- * the only mutable host state is an atomic counter that picks the workspace
- * region.
+ * the only mutable host state is the mutex-guarded table that assigns the
+ * workspace regions to streams.
  *
  * Preconditions (the page's host-side rule that K and N be multiples of 4 for
  * the 16-byte vector loads, "Önemli Optimizasyonlar" §1):
@@ -77,7 +84,8 @@ extern "C" {
 #define GEMM_ERR_DTYPE (-4)  /* unknown flag bits or w_dtype */
 #define GEMM_ERR_ALIAS (-5)  /* Y overlaps an input */
 #define GEMM_ERR_LAUNCH (-6) /* the HIP runtime reported an error at launch */
-#define GEMM_ERR_CONFIG (-7) /* an explicit tile configuration index is out of range */
+#define GEMM_ERR_CONFIG (-7) /* an explicit tile configuration index is out of range, or it splits K and
+                                the shape exceeds the workspace or the stream has no workspace region */
 
 /* gemm_fwd flags. */
 #define GEMM_FLAG_W_F16 0x1u /* W holds IEEE binary16 values; otherwise fp32 */

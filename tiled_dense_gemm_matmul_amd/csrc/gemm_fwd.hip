@@ -51,7 +51,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_fwd.h"
@@ -83,8 +83,9 @@ struct Params {
 // bumps the tile's counter; the last to arrive adds the KS slots in the fixed
 // order 0..KS-1 (so results do not depend on arrival order), adds R, writes
 // Y and resets the counter.  Static storage, zero at load, so no call
-// allocates; calls rotate over kSkRegions regions, so up to that many
-// split-K calls may be in flight at once on one device.
+// allocates.  The kSkRegions regions belong to streams (stream_region):
+// calls on one stream run in order and share their stream's region, and
+// calls on different streams never share one.
 constexpr int kSkRegions = 4;
 constexpr int kSkMaxSplit = 8;
 constexpr int kSkMaxElems = 1 << 19;   // M * N limit for split-K calls
@@ -1042,7 +1043,22 @@ bool split_fits(const ConfigEntry &e, int64_t M, int64_t N) {
     return M * N <= kSkMaxElems && ceil_div(M, e.bm) * ceil_div(N, e.bn) <= kSkMaxTiles;
 }
 
-std::atomic<unsigned> g_region_ticket{0};
+// Split-K workspace regions, one per stream: each of the first kSkRegions
+// distinct streams that make a split-K call keeps a region for the life of
+// the process (calls on one stream run in order, so they can share it).
+// Returns -1 when every region belongs to another stream.
+std::mutex g_region_mu;
+void *g_region_owner[kSkRegions];
+int g_regions_taken = 0;
+
+int stream_region(void *stream) {
+    std::lock_guard<std::mutex> lock(g_region_mu);
+    for (int r = 0; r < g_regions_taken; ++r)
+        if (g_region_owner[r] == stream) return r;
+    if (g_regions_taken == kSkRegions) return -1;
+    g_region_owner[g_regions_taken] = stream;
+    return g_regions_taken++;
+}
 
 int table_index(const ConfigEntry *table, int count, const char *name) {
     for (int i = 0; i < count; ++i) {
@@ -1060,7 +1076,9 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // 64 x 384 tile re-stages (and recombines) each block of A rows half as
 // often as 128 x 192 at the same MFMA work per wave: 297 against 310 us at
 // 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.
-int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
+// `split` false: only configurations without split-K (for a stream that has
+// no workspace region).
+int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split = true) {
     (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
     static const int swiglu_wide = config_index("64x384x32_w1x4_sp8_pf4_il");
@@ -1085,7 +1103,7 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
     if (M <= 128) return tiny;
     if (K >= 2048) {
         // long K on a small grid: split K in two when the workspace holds it
-        if (split_fits(kConfigs[deep_split], M, N) && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
+        if (split && split_fits(kConfigs[deep_split], M, N) && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
             return deep_split;
         return deep;
     }
@@ -1106,8 +1124,9 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16) {
 // transposed A come to between one and two per CU while 48 x 48 tiles come
 // to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
 // at 768 x 512 x 768.
-int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
+int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split = true) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4");
+    static const int fwd_deep = config_index("16x96x64_k4_sp8_pf3_il");
     static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
     static const int tiny = table_index(kBwdConfigs, kNumBwdConfigs, "16x48x128_k4_sp4_dAW");
@@ -1117,11 +1136,13 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
     // the forward rule without its SwiGLU tile, which the backward table
     // does not hold
     (void)swiglu;
-    const int f = select_config(M, K, N, 0, 0);
+    const int f = select_config(M, K, N, 0, 0, split);
     if (f < 0) return -1;
     if (op == kOpTN && f == fwd_mid) return small;
-    if (op == kOpNT && f == fwd_deep_split && K <= 4096) return tiny;
-    if (op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
+    // without split-K the forward rule's long-K choice is the deep tile
+    const bool long_k_grid = f == fwd_deep_split || (!split && f == fwd_deep);
+    if (op == kOpNT && long_k_grid && K <= 4096) return tiny;
+    if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
         return long_k;
     const int r = table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
@@ -1179,10 +1200,17 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
 
-    const int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
+    int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
     if (cfg < 0 || cfg >= kNumConfigs) return GEMM_ERR_CONFIG;
+    int region = 0;
+    if (kConfigs[cfg].ks > 1) {
+        if (!split_fits(kConfigs[cfg], M, N)) return GEMM_ERR_CONFIG;
+        region = stream_region(stream);
+        if (region < 0 && config >= 0) return GEMM_ERR_CONFIG;
+        if (region < 0) cfg = select_config(M, K, N, swiglu, w16, false);
+        if (cfg < 0) return GEMM_ERR_CONFIG;
+    }
     const ConfigEntry &e = kConfigs[cfg];
-    if (e.ks > 1 && !split_fits(e, M, N)) return GEMM_ERR_CONFIG;
     Params p;
     p.A = A; p.U = U; p.W = W; p.R = R; p.Y = Y;
     p.EG = nullptr; p.EU = nullptr; p.Y2 = nullptr;
@@ -1191,7 +1219,7 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     p.tiles_n = (int)ceil_div(N, e.bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     p.kchunk = (int)(ceil_div(ceil_div(K, e.ks), e.bk) * e.bk);
-    p.region = e.ks > 1 ? (int)(g_region_ticket.fetch_add(1u, std::memory_order_relaxed) % kSkRegions) : 0;
+    p.region = region;
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
@@ -1259,10 +1287,17 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
         hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, nullptr, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
-    const int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu);
+    int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu);
     if (cfg < 0 || cfg >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
+    int region = 0;
+    if (kBwdConfigs[cfg].ks > 1) {
+        if (!split_fits(kBwdConfigs[cfg], km, kn2)) return GEMM_ERR_CONFIG;
+        region = stream_region(stream);
+        if (region < 0 && config >= 0) return GEMM_ERR_CONFIG;
+        if (region < 0) cfg = select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu, false);
+        if (cfg < 0) return GEMM_ERR_CONFIG;
+    }
     const ConfigEntry &e = kBwdConfigs[cfg];
-    if (e.ks > 1 && !split_fits(e, km, kn2)) return GEMM_ERR_CONFIG;
     Params p;
     p.A = A; p.U = U; p.W = B; p.R = acc ? Y : nullptr; p.Y = Y;
     p.EG = EG; p.EU = EU; p.Y2 = Y2;
@@ -1271,7 +1306,7 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
     p.tiles_n = (int)ceil_div(kn2, e.bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     p.kchunk = (int)(ceil_div(ceil_div(kk, e.ks), e.bk) * e.bk);
-    p.region = e.ks > 1 ? (int)(g_region_ticket.fetch_add(1u, std::memory_order_relaxed) % kSkRegions) : 0;
+    p.region = region;
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[op == kOpTN ? 1 : 0][swiglu ? 1 : 0][acc ? 1 : 0];
