@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the step: run the MFMA ceiling probe (independent fp32 MFMAs only) at 4, 8 "
                          "and 16 waves per CU and print the sustained TFLOP/s and engine clock")
+    ap.add_argument("--shards", action="store_true",
+                    help="instead of the step: time each product at the per-GPU shape of its natural sharding "
+                         "over 2, 4 and 8 GPUs (lm_head and gate/up by columns, the SwiGLU down-projection by "
+                         "its contraction), one GPU standing in for one shard")
     ap.add_argument("--counters-from", metavar="DIR",
                     help="turn the rocprofv3 counter runs under DIR (p1/, p2/) into "
                          + os.path.relpath(os.path.join(ROOT, "profiles", "seq512_counters.md"), ROOT) + " and exit")
@@ -702,8 +706,79 @@ def time_configs():
     print(f"\ncfg1 amortised over 1000 back-to-back launches: {c1['amortised_us_per_launch']} us per launch")
 
 
+SHARDS = [
+    # product, M, K, N, sharded dimension, swiglu, w16, residual
+    ("lm_head, 16 x 512 tokens", 8192, 768, 50304, "N", False, True, False),
+    ("lm_head, seq 512", 512, 768, 16384, "N", False, True, False),
+    ("ffn_gate_up, 16 x 512 tokens", 8192, 768, 3072, "N", False, True, False),
+    ("ffn_down SwiGLU, 16 x 512 tokens", 8192, 3072, 768, "K", True, True, True),
+    ("ffn_down SwiGLU, seq 512 (fp32 W)", 512, 3072, 768, "K", True, False, True),
+]
+
+
+def time_shards():
+    """Each product at the shape one GPU holds when it is sharded over g GPUs
+    without changing the kernel: column-parallel weights split N, and the
+    down-projection, whose G and U arrive split along d_ff, splits K (its
+    partial outputs would then be summed across GPUs, which is not timed
+    here).  Per launch, events recorded by the launch itself, as for the
+    workload configurations; the last column compares g shards' time with
+    the whole product's: t(1) / (g t(g))."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    sp = st.cuda_stream
+    lines = ["| product | GPUs | shard M×K×N | tile | warm median µs | TFLOP/s | % of 157.3 | t(1) / (g·t(g)) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for seed, (name, M0, K0, N0, dim, swiglu, w16, resid) in enumerate(SHARDS):
+        t1 = None
+        for g in (1, 2, 4, 8):
+            M, K, N = M0, (K0 // g if dim == "K" else K0), (N0 // g if dim == "N" else N0)
+            c = inputs.random_case(900 + seed, M, K, N, swiglu=swiglu, w16=w16, residual=resid)
+            d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in c.items()}
+            Y = torch.empty((M, N), device=dev)
+            R = d.get("R")
+
+            def launch(ev=(None, None)):
+                if swiglu:
+                    return lib.gemm_fwd_swiglu_timed(d["G"].data_ptr(), d["U"].data_ptr(), d["W"].data_ptr(),
+                                                     R.data_ptr(), Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+                return lib.gemm_fwd_timed(d["X"].data_ptr(), d["W"].data_ptr(), None if R is None else R.data_ptr(),
+                                          Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.2:
+                for _ in range(10):
+                    assert launch() == 0
+                torch.cuda.synchronize()
+            n = 30 if M * N * K > 1e11 else 100
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a, b in evs:
+                a.record(st)
+                b.record(st)
+            torch.cuda.synchronize()
+            for a, b in evs:
+                assert launch((a.cuda_event, b.cuda_event)) == 0
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            t1 = us if g == 1 else t1
+            tf = 2 * M * N * K / us / 1e6
+            tile = binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16)
+            lines.append(f"| {name} | {g} | {M}×{K}×{N} | {tile} | {us:.2f} | {tf:.1f} | "
+                         f"{100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f} | {t1 / (g * us):.2f} |")
+            print(lines[-1], file=sys.stderr, flush=True)
+            del d, Y, R
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.shards:
+        time_shards()
+        return
     if args.configs:
         import torch
         torch.backends.cuda.matmul.allow_tf32 = False

@@ -83,6 +83,22 @@ def test_config_table(lib):
             for w16 in (0, 1):
                 assert 0 <= lib.gemm_select_config(*shape, sw, w16) < n
 
+    def pick(M, K, N, sw, w16):
+        return lib.gemm_config_name(lib.gemm_select_config(M, K, N, sw, w16)).decode()
+    # the workload configurations (their tiles are the ones bench.py times)
+    assert pick(128, 768, 768, 0, 0) == "16x48x128_k4_sp4_dAW"
+    assert pick(512, 768, 768, 0, 0) == "32x48x64_k4_sp4_pf3_dAW"
+    assert pick(512, 3072, 768, 1, 0) == "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
+    assert pick(512, 768, 16384, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    assert pick(512, 768, 3072, 0, 1) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert pick(8192, 3072, 768, 1, 1) == "64x384x32_w1x4_sp8_pf4_il"
+    assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    # mid-size grids: 128 x 64 while it gives two tiles per CU, 64 x 64 when
+    # it fills one whole round and 64 x 48 does not
+    assert pick(512, 768, 8192, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert pick(512, 768, 2048, 0, 1) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(512, 768, 4096, 0, 1) == "64x64x64_w2x2_sp4_dAW"
+
 
 # fake, well-aligned, non-overlapping host addresses
 X, W, R, Y, U = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
@@ -212,6 +228,9 @@ def test_backward_selection(lib):
     assert name(2, 512, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
     assert name(2, 512, 3072, 768) == "32x48x64_k4_sp4_pf3_dAW"
     assert name(1, 512, 768, 16384) == "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"
+    assert name(1, 512, 3072, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert name(1, 512, 768, 3072) == "16x48x128_k4_sp4_dAW"
+    assert name(2, 512, 768, 16384) == "128x128x32_w2x2_sp4_pf3_il_dA"
 
 
 def test_loss_exports_and_validation(lib):

@@ -990,6 +990,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<64, 384, 32, 1, 4, 1, 8, 4, 1, 1>>("64x384x32_w1x4_sp8_pf4_il"),
+    make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
     make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("32x48x64_k4_sp8_pf3_il_ks2"),
@@ -1075,15 +1076,21 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // with the K range split over waves for small grids.  With SwiGLU, a
 // 64 x 384 tile re-stages (and recombines) each block of A rows half as
 // often as 128 x 192 at the same MFMA work per wave: 297 against 310 us at
-// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.
+// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.  Grids too
+// small for those take 128 x 64 tiles while they still come to two per CU
+// (512 x 768 x 8192: 51.6 against 56.8 us for 64 x 64), and 64 x 64 tiles
+// rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
+// and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
 // `split` false: only configurations without split-K (for a stream that has
-// no workspace region).
-int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split = true) {
+// no workspace region).  `forward` false: the rule as the backward products
+// measured it, without the 128 x 64 tile and the whole-round 64 x 64 choice.
+int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split = true, bool forward = true) {
     (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
     static const int swiglu_wide = config_index("64x384x32_w1x4_sp8_pf4_il");
     static const int wide = config_index("128x192x32_w2x2_sp8_pf4_il");
-    static const int mid = config_index("64x64x64_w2x2_sp4");
+    static const int tall = config_index("128x64x32_w2x2_sp4_pf3_il_dA");
+    static const int mid = config_index("64x64x64_w2x2_sp4_dAW");
     static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il_dA");
     static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
@@ -1091,15 +1098,18 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     static const int tiny = config_index("16x48x128_k4_sp4_dAW");
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
-    static const bool complete = big >= 0 && swiglu_wide >= 0 && wide >= 0 && mid >= 0 && narrow >= 0 &&
-                                 small >= 0 && deep >= 0 && deep_split >= 0 && tiny >= 0;
+    static const bool complete = big >= 0 && swiglu_wide >= 0 && wide >= 0 && tall >= 0 && mid >= 0 &&
+                                 narrow >= 0 && small >= 0 && deep >= 0 && deep_split >= 0 && tiny >= 0;
     if (!complete) return -1;
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
     if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return swiglu_wide;
     if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
-    if (ceil_div(M, 64) * ceil_div(N, 64) >= 2 * cus) return mid;
-    if (ceil_div(M, 64) * ceil_div(N, 48) >= cus) return narrow;
+    if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return tall;
+    const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
+    if (t64 >= 2 * cus) return mid;
+    if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return mid;
+    if (t48 >= cus) return narrow;
     if (M <= 128) return tiny;
     if (K >= 2048) {
         // long K on a small grid: split K in two when the workspace holds it
@@ -1125,7 +1135,8 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
 // at 768 x 512 x 768.
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split = true) {
-    static const int fwd_mid = config_index("64x64x64_w2x2_sp4");
+    static const int fwd_mid = config_index("64x64x64_w2x2_sp4_dAW");
+    static const int mid = table_index(kBwdConfigs, kNumBwdConfigs, "64x64x64_w2x2_sp4");
     static const int fwd_deep = config_index("16x96x64_k4_sp8_pf3_il");
     static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
@@ -1133,10 +1144,10 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     static const int long_k = table_index(kBwdConfigs, kNumBwdConfigs, "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
     static const int square = table_index(kBwdConfigs, kNumBwdConfigs, "48x48x64_k4_sp4_pf3_dAW");
     const int64_t cus = 256;
-    // the forward rule without its SwiGLU tile, which the backward table
-    // does not hold
+    // the forward rule without its SwiGLU and forward-only tiles, which the
+    // backward table does not hold
     (void)swiglu;
-    const int f = select_config(M, K, N, 0, 0, split);
+    const int f = select_config(M, K, N, 0, 0, split, false);
     if (f < 0) return -1;
     if (op == kOpTN && f == fwd_mid) return small;
     // without split-K the forward rule's long-K choice is the deep tile
@@ -1145,7 +1156,8 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
         return long_k;
-    const int r = table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    // the backward table holds the 64 x 64 tile with register staging
+    const int r = f == fwd_mid ? mid : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
     if (op == kOpTN && r == small) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
         if (t32 > cus && t32 < 2 * cus && t48 <= cus) return square;
