@@ -98,6 +98,8 @@ def test_config_table(lib):
     assert pick(512, 768, 8192, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert pick(512, 768, 2048, 0, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(512, 768, 4096, 0, 1) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(8192, 768, 768, 0, 0) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert pick(8192, 3072, 768, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
 
 
 # fake, well-aligned, non-overlapping host addresses

@@ -1076,9 +1076,12 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // with the K range split over waves for small grids.  With SwiGLU, a
 // 64 x 384 tile re-stages (and recombines) each block of A rows half as
 // often as 128 x 192 at the same MFMA work per wave: 297 against 310 us at
-// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.  Grids too
-// small for those take 128 x 64 tiles while they still come to two per CU
-// (512 x 768 x 8192: 51.6 against 56.8 us for 64 x 64), and 64 x 64 tiles
+// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.  Other grids
+// too small for 128 x 128 take 128 x 64 tiles while those come to two per
+// CU: 512 x 768 x 8192 in 51.6 us against 56.8 for 64 x 64; 8192 x 768 x 768
+// in 77 against 86 us (f16 W) and 75 against 79 (fp32 W with R) for
+// 128 x 192; 8192 x 3072 x 768 with f16 W in 279 against 295; never slower
+// than 128 x 192 on the shapes measured.  And 64 x 64 tiles
 // rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
 // and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
 // `split` false: only configurations without split-K (for a stream that has
@@ -1104,8 +1107,10 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
     if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return swiglu_wide;
-    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
+    // forward products: 128 x 64 wherever that gives two tiles per CU, which
+    // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
     if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return tall;
+    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
     if (t64 >= 2 * cus) return mid;
     if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return mid;
