@@ -124,6 +124,13 @@ BACKWARD = [
     ("ffn_gate_up dW", "matmul_at_acc", 512, 768, 3072),
     ("ffn_down dW (SwiGLU recomputed)", "matmul_at_swiglu_a", 512, 3072, 768),
     ("lm_head dW", "matmul_at", 512, 768, 16384),
+    # the 16 x 512-token batch
+    ("qkvo dX, 8192 tokens", "matmul_t", 8192, 768, 768),
+    ("ffn_down dH, 8192 tokens", "matmul_t", 8192, 3072, 768),
+    ("ffn_gate_up dX, 8192 tokens", "matmul_t_acc", 8192, 768, 3072),
+    ("qkvo dW, 8192 tokens", "matmul_at", 8192, 768, 768),
+    ("ffn_gate_up dW, 8192 tokens", "matmul_at_acc", 8192, 768, 3072),
+    ("ffn_down dW (SwiGLU recomputed), 8192 tokens", "matmul_at_swiglu_a", 8192, 3072, 768),
 ]
 
 

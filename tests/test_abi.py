@@ -233,6 +233,12 @@ def test_backward_selection(lib):
     assert name(1, 512, 3072, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(1, 512, 768, 3072) == "16x48x128_k4_sp4_dAW"
     assert name(2, 512, 768, 16384) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    # 16 x 512 tokens
+    assert name(1, 8192, 768, 768) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert name(1, 8192, 768, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert name(1, 8192, 3072, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 8192, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
 
 
 def test_loss_exports_and_validation(lib):
