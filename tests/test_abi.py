@@ -239,6 +239,10 @@ def test_backward_selection(lib):
     assert name(1, 8192, 3072, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
     assert name(2, 8192, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
+    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1)).decode() == \
+        "96x96x64_w2x2_sp4_pf3_il_dA"
+    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1)).decode() == \
+        "32x48x64_k4_sp4_pf3_dAW"
 
 
 def test_loss_exports_and_validation(lib):

@@ -1036,6 +1036,9 @@ const ConfigEntry kBwdConfigs[] = {
     // a transposed B whose grid of 128 x 64 tiles comes to two per CU
     // (the 8192-token dX of the attention projections and of gate/up)
     make_bwd_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
+    // the SwiGLU weight gradient over a long contraction: G and U re-staged
+    // once per 96 output columns instead of once per 48
+    make_bwd_entry<Tile<96, 96, 64, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("96x96x64_w2x2_sp4_pf3_il_dA"),
 };
 constexpr int kNumBwdConfigs = sizeof(kBwdConfigs) / sizeof(kBwdConfigs[0]);
 
@@ -1145,7 +1148,10 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // forward rule picks at 768 x 8192 x 768 (whose output is too large for the
 // split-K workspace).  A transposed B takes 128 x 64 tiles where they come to
 // two per CU and 128 x 128 tiles do not: 74 against 80 us at 8192 x 768 x 768
-// and 282 against over 300 at 8192 x 3072 x 768.
+// and 282 against over 300 at 8192 x 3072 x 768.  The SwiGLU weight gradient
+// over a contraction of 4096 or more takes 96 x 96 tiles where they fill the
+// CUs, combining G and U half as often: 346 against 364 us at
+// 3072 x 8192 x 768.
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split = true) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4_dAW");
     static const int mid = table_index(kBwdConfigs, kNumBwdConfigs, "64x64x64_w2x2_sp4");
@@ -1156,23 +1162,26 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     static const int long_k = table_index(kBwdConfigs, kNumBwdConfigs, "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
     static const int square = table_index(kBwdConfigs, kNumBwdConfigs, "48x48x64_k4_sp4_pf3_dAW");
     static const int tall = table_index(kBwdConfigs, kNumBwdConfigs, "128x64x32_w2x2_sp4_pf3_il_dA");
+    static const int swiglu_sq = table_index(kBwdConfigs, kNumBwdConfigs, "96x96x64_w2x2_sp4_pf3_il_dA");
     const int64_t cus = 256;
     // the forward rule without its SwiGLU and forward-only tiles, which the
     // backward table does not hold
-    (void)swiglu;
     const int f = select_config(M, K, N, 0, 0, split, false);
     if (f < 0) return -1;
     if (op == kOpNT && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus && ceil_div(M, 128) * ceil_div(N, 128) < 2 * cus)
         return tall;
-    if (op == kOpTN && f == fwd_mid) return small;
     // without split-K the forward rule's long-K choice is the deep tile
     const bool long_k_grid = f == fwd_deep_split || (!split && f == fwd_deep);
     if (op == kOpNT && long_k_grid && K <= 4096) return tiny;
     if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
         return long_k;
-    // the backward table holds the 64 x 64 tile with register staging
-    const int r = f == fwd_mid ? mid : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    // a transposed A takes 32 x 48 tiles where the forward rule takes 64 x 64
+    // (whose backward form stages with registers)
+    const int r = f == fwd_mid ? (op == kOpTN ? small : mid)
+                               : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
+    if (op == kOpTN && swiglu && r == small && K >= 4096 && ceil_div(M, 96) * ceil_div(N, 96) >= cus)
+        return swiglu_sq;
     if (op == kOpTN && (r == small || f == fwd_deep)) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
         if (t32 > cus && t32 < 2 * cus && t48 <= cus) return square;
