@@ -45,9 +45,9 @@
  * a split-K call each keep a region for the life of the process, and calls
  * on one stream, which run in order, share it (the four are counted over all
  * devices of the process, though each device has its own workspace).  Calls
- * on a later stream get
- * no region: the library's own tile choice then takes a configuration
- * without split-K (same results within the tolerance, not bit for bit), and
+ * on a later stream get no region: the library's own tile choice then takes
+ * a configuration without split-K (same results within the tolerance, not
+ * bit for bit), and
  * an explicit split-K configuration gives GEMM_ERR_CONFIG.  So split-K calls
  * on different streams never share workspace.  The special per-thread
  * default stream handle counts as a single stream: callers that use it from
