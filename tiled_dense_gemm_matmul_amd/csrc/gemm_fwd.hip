@@ -448,12 +448,23 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         if constexpr (DMA_A) {
             const int arem = abytes - k0 * 4;
             const Rsrc rA = make_rsrc(Abase + k0, arem > 0 ? arem : 0);
+            // a stage wholly inside the K range needs no per-item check
+            // (krem is uniform, so this is a scalar branch)
+            if (krem >= BK) {
 #pragma unroll
-            for (int j = 0; j < A_DIT; ++j) {
-                const int c = pw + j * NPW;
-                if (A_CH % NPW != 0 && c >= A_CH) break;
-                const int off = ad_gk[j] < krem ? ad_off[j] : kOOB;
-                load_f32x4_to_lds(rA, S + c * 256, off);
+                for (int j = 0; j < A_DIT; ++j) {
+                    const int c = pw + j * NPW;
+                    if (A_CH % NPW != 0 && c >= A_CH) break;
+                    load_f32x4_to_lds(rA, S + c * 256, ad_off[j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < A_DIT; ++j) {
+                    const int c = pw + j * NPW;
+                    if (A_CH % NPW != 0 && c >= A_CH) break;
+                    const int off = ad_gk[j] < krem ? ad_off[j] : kOOB;
+                    load_f32x4_to_lds(rA, S + c * 256, off);
+                }
             }
         }
         if constexpr (DMA_W) {
