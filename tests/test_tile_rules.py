@@ -1,0 +1,85 @@
+"""Parity in the configurations that the tile-choice rules for mid-size and
+batch-size grids pick (each test first checks that the rule picked it):
+the forward 128 x 64 and 64 x 64 tiles, and the backward 128 x 64 (transposed
+B), 48 x 48 (long-contraction dW) and 96 x 96 (SwiGLU dW over a long
+contraction) tiles.  Large outputs are compared on sampled rows that include
+the last tile's rows."""
+import numpy as np
+import pytest
+
+import oracle
+from tiled_dense_gemm_matmul_amd import inputs
+
+from _gpu import check, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(M, seed, count=48, tail=128):
+    rng = np.random.default_rng(seed)
+    start = max(M - tail, 0)
+    return np.unique(np.concatenate([rng.choice(max(start, 1), size=min(count, max(start, 1)), replace=False),
+                                     np.arange(start, M)])).astype(np.int64)
+
+
+@pytest.mark.parametrize("M,K,N,w16,resid,tile", [
+    (512, 768, 8192, True, False, "128x64x32_w2x2_sp4_pf3_il_dA"),
+    (8192, 768, 768, False, True, "128x64x32_w2x2_sp4_pf3_il_dA"),
+    (512, 768, 2048, True, False, "64x64x64_w2x2_sp4_dAW"),
+])
+def test_forward_rule(M, K, N, w16, resid, tile):
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.kernel_config(M, K, N, w16=w16) == tile
+    say(f"forward {M}x{K}x{N} w16={w16} R={resid} -> {tile}")
+    c = inputs.random_case(1000 + M + N, M, K, N, w16=w16, residual=resid)
+    y = run(c).cpu().numpy()
+    rows = _rows(M, 7)
+    check(c, y[rows], rows=rows, label=f"{M}x{K}x{N} {tile}")
+
+
+def _cmp(y, ref, scale, label):
+    res = oracle.compare(y, ref, scale, oracle.TOL_W32)
+    say(f"  {label}: max err/tol {res['max_ratio']:.4g}, fails {res['fails']} of {res['n']}")
+    assert res["fails"] == 0, res
+
+
+def test_backward_matmul_t_128x64():
+    # dX = dY @ W^T for 8192 tokens, 768 outputs, 768 inputs
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    M, K, N = 8192, 768, 768
+    assert binding.bwd_kernel_config("matmul_t", M, K, N) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    c = inputs.backward_case(11, M, K, N)
+    dX = binding.matmul_t(to_dev(c["dY"]), to_dev(c["W"]))
+    torch.cuda.synchronize()
+    rows = _rows(M, 8)
+    ref, scale = oracle.matmul_t(c["dY"], c["W"], rows=rows, want_scale=True)
+    _cmp(dX.cpu().numpy()[rows], ref, scale, "matmul_t 8192x768x768")
+
+
+def test_backward_matmul_at_48x48_long_contraction():
+    # dW = X^T @ dY over 8192 tokens: 768 x 768, too large for the split-K workspace
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    M, K, N = 8192, 768, 768
+    assert binding.bwd_kernel_config("matmul_at", M, K, N) == "48x48x64_k4_sp4_pf3_dAW"
+    c = inputs.backward_case(12, M, K, N)
+    dW = binding.matmul_at(to_dev(c["X"]), to_dev(c["dY"]))
+    torch.cuda.synchronize()
+    rows = _rows(K, 9, count=32, tail=48)
+    ref, scale = oracle.matmul_at(c["X"], c["dY"], rows=rows, want_scale=True)
+    _cmp(dW.cpu().numpy()[rows], ref, scale, "matmul_at 8192x768x768")
+
+
+def test_backward_swiglu_dw_96x96():
+    # dW_down = (silu(G) * U)^T @ dY over 8192 tokens: 3072 x 768
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    M, K, N = 8192, 3072, 768
+    assert binding.bwd_kernel_config("matmul_at", M, K, N, swiglu=True) == "96x96x64_w2x2_sp4_pf3_il_dA"
+    c = inputs.backward_case(13, M, K, N, swiglu=True)
+    dW = binding.matmul_at_swiglu_a(to_dev(c["G"]), to_dev(c["U"]), to_dev(c["dY"]))
+    torch.cuda.synchronize()
+    rows = _rows(K, 10, count=24, tail=96)
+    ref, scale = oracle.matmul_at(c["G"], c["dY"], U=c["U"], rows=rows, want_scale=True)
+    _cmp(dW.cpu().numpy()[rows], ref, scale, "matmul_at_swiglu_a 8192x3072x768")
