@@ -238,7 +238,8 @@ def test_backward_selection(lib):
     assert name(1, 8192, 768, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 8192, 3072, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
-    assert name(2, 8192, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 8192, 768, 3072) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 8192, 1024, 4096) == "32x48x64_k4_sp4_pf3_dAW"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1)).decode() == \
         "96x96x64_w2x2_sp4_pf3_il_dA"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1)).decode() == \

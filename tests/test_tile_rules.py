@@ -57,18 +57,19 @@ def test_backward_matmul_t_128x64():
     _cmp(dX.cpu().numpy()[rows], ref, scale, "matmul_t 8192x768x768")
 
 
-def test_backward_matmul_at_48x48_long_contraction():
-    # dW = X^T @ dY over 8192 tokens: 768 x 768, too large for the split-K workspace
+@pytest.mark.parametrize("M,K,N", [(8192, 768, 768), (8192, 768, 3072)])
+def test_backward_matmul_at_48x48_long_contraction(M, K, N):
+    # dW = X^T @ dY over 8192 tokens: 768 x 768 (too large for the split-K
+    # workspace) and 768 x 3072 (whole 48 x 48 tiles)
     import torch
     from tiled_dense_gemm_matmul_amd import binding
-    M, K, N = 8192, 768, 768
     assert binding.bwd_kernel_config("matmul_at", M, K, N) == "48x48x64_k4_sp4_pf3_dAW"
-    c = inputs.backward_case(12, M, K, N)
+    c = inputs.backward_case(12 + N, M, K, N)
     dW = binding.matmul_at(to_dev(c["X"]), to_dev(c["dY"]))
     torch.cuda.synchronize()
     rows = _rows(K, 9, count=32, tail=48)
     ref, scale = oracle.matmul_at(c["X"], c["dY"], rows=rows, want_scale=True)
-    _cmp(dW.cpu().numpy()[rows], ref, scale, "matmul_at 8192x768x768")
+    _cmp(dW.cpu().numpy()[rows], ref, scale, f"matmul_at {M}x{K}x{N}")
 
 
 def test_backward_swiglu_dw_96x96():

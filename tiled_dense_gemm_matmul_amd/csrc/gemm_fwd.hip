@@ -1162,7 +1162,11 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // and 282 against over 300 at 8192 x 3072 x 768.  The SwiGLU weight gradient
 // over a contraction of 4096 or more takes 96 x 96 tiles where they fill the
 // CUs, combining G and U half as often: 346 against 364 us at
-// 3072 x 8192 x 768.
+// 3072 x 8192 x 768.  Other weight gradients over a contraction of 4096 or
+// more take 48 x 48 tiles too where the output splits into whole ones:
+// 311 against 331 us at 3072 x 8192 x 768, 610 against 638 at
+// 768 x 16384 x 3072 (with ragged 48-row tiles, 1024 x 8192 x 4096, they
+// lose 3%).
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split = true) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4_dAW");
     static const int mid = table_index(kBwdConfigs, kNumBwdConfigs, "64x64x64_w2x2_sp4");
@@ -1196,6 +1200,8 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     if (op == kOpTN && (r == small || f == fwd_deep)) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
         if (t32 > cus && t32 < 2 * cus && t48 <= cus) return square;
+        // long contractions whose output splits into whole 48 x 48 tiles
+        if (r == small && K >= 4096 && M % 48 == 0 && N % 48 == 0 && t48 >= cus) return square;
     }
     return r;
 }
