@@ -225,7 +225,9 @@ int gemm_num_configs(void);
 /* Static name of a configuration ("BMxBNxBK_..."), or NULL if out of range. */
 const char *gemm_config_name(int config);
 
-/* The configuration the library picks for a shape (swiglu, w_f16 are 0/1). */
+/* The configuration the library picks for a shape (swiglu, w_f16 are 0/1),
+ * on a stream that holds a split-K workspace region (a stream without one
+ * gets the choice without split-K instead). */
 int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16);
 
 /* Static text for a status code. */
