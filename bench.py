@@ -813,8 +813,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the kernels have no multi-GPU path "
-              "(the GEMMs shard by rows or by columns with no exchange between GPUs)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "`bench.py --shards` times each product at the shape one GPU would hold", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
