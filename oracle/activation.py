@@ -19,6 +19,7 @@ import numpy as np
 
 SQRT_2_OVER_PI = 0.7978845608028654     # sqrt(2 / pi)
 GELU_COEFF = 0.044715
+GELU_CLAMP = 100.0                      # input clamp before the cube
 
 
 def nan_guard(x):
@@ -48,13 +49,13 @@ def gelu(x):
     """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); the cube is taken of
     x clamped to [-100, 100], where tanh is already +-1."""
     x = np.asarray(x, dtype=np.float64)
-    xc = np.clip(x, -100.0, 100.0)
+    xc = np.clip(x, -GELU_CLAMP, GELU_CLAMP)
     inner = SQRT_2_OVER_PI * (xc + GELU_COEFF * xc ** 3)
     return 0.5 * x * (1.0 + np.tanh(inner))
 
 
 def gelu_derivative(x_in):
-    x = np.clip(np.asarray(x_in, dtype=np.float64), -100.0, 100.0)
+    x = np.clip(np.asarray(x_in, dtype=np.float64), -GELU_CLAMP, GELU_CLAMP)
     inner = SQRT_2_OVER_PI * (x + GELU_COEFF * x ** 3)
     t = np.tanh(inner)
     sech2 = 1.0 - t * t
@@ -81,7 +82,7 @@ def ffn_swiglu_backward(grad_hidden, gate, up):
 def ffn_gelu_backward(grad_hidden, pre_gelu):
     """(grad_pre, scale): grad_pre = nan_guard(g gelu'(pre))."""
     g = np.asarray(grad_hidden, dtype=np.float64)
-    x = np.clip(np.asarray(pre_gelu, dtype=np.float64), -100.0, 100.0)
+    x = np.clip(np.asarray(pre_gelu, dtype=np.float64), -GELU_CLAMP, GELU_CLAMP)
     with np.errstate(invalid="ignore", over="ignore"):
         return _gelu_backward(g, x, pre_gelu)
 
@@ -89,9 +90,28 @@ def ffn_gelu_backward(grad_hidden, pre_gelu):
 def _gelu_backward(g, x, pre_gelu):
     inner = SQRT_2_OVER_PI * (x + GELU_COEFF * x ** 3)
     t = np.tanh(inner)
+    sech2 = 1.0 - t * t
     d_inner = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_COEFF * x * x)
-    mag = np.abs(g) * (1.0 + np.abs(x) * d_inner) * (1.0 + (1.0 - t * t) * _inner_mag(x))
+    im = _inner_mag(x)
+    # 0.5 (1 + t): t's rounding, and the argument's (sech^2 times a few ulps
+    # of |inner|); 0.5 x sech^2 d_inner: sech^2 = 1 - t^2 is computed with an
+    # absolute error of a few ulps of 1 while tanh is short of +-1 in fp32,
+    # and exactly (0) once it is +-1, which happens where the true sech^2
+    # falls far below 2^-24: the floor is weighted by _unsaturated(sech^2).
+    mag = np.abs(g) * (0.5 * (1.0 + np.abs(t)) * (1.0 + sech2 * im)
+                       + 0.5 * np.abs(x) * d_inner * (sech2 * (1.0 + im) + SECH2_FLOOR * _unsaturated(sech2)))
     return nan_guard(g * gelu_derivative(pre_gelu)), nan_guard(mag)
+
+
+def _unsaturated(sech2):
+    """1 where fp32 tanh may still be an ulp short of +-1, falling to 0 with
+    sech^2 beyond.  A correctly rounded tanh reaches +-1 once sech^2 is
+    below about 2^-24; a faithfully rounded one (1 ulp) can stay an ulp
+    short a little further (numpy's float32 tanh does so at |inner| = 10,
+    sech^2 = 8e-9), so the floor is kept whole down to sech^2 = 2^-36
+    (|inner| about 13) and decays with sech^2 below that.  At |x| >= 9
+    (|inner| >= 33) it is below 1e-17."""
+    return np.minimum(1.0, sech2 * 2.0 ** 36)
 
 
 def _inner_mag(x):
@@ -101,19 +121,27 @@ def _inner_mag(x):
 
 
 def gelu_inplace(x):
-    """(gelu(x), scale)."""
+    """(gelu(x), scale).  The scale collapses with 1 + t where tanh
+    saturates at -1 (the result is 0 there, exactly in fp32 too): 1 + t is
+    short by t's rounding only while fp32 tanh is not yet -1."""
     x64 = np.asarray(x, dtype=np.float64)
-    xc = np.clip(x64, -100.0, 100.0)
+    xc = np.clip(x64, -GELU_CLAMP, GELU_CLAMP)
     t = np.tanh(SQRT_2_OVER_PI * (xc + GELU_COEFF * xc ** 3))
-    return gelu(x64), np.abs(x64) * (1.0 + (1.0 - t * t) * _inner_mag(xc))
+    sech2 = 1.0 - t * t
+    scale = 0.5 * np.abs(x64) * ((1.0 + t) + sech2 * _inner_mag(xc) + T_FLOOR * _unsaturated(sech2))
+    return gelu(x64), scale
 
 
 # |x - x_ref| <= rel * scale + abs.  The scales are the magnitudes of the
 # terms before they cancel, not of the result: in fp32 the page's GeLU
-# formulas lose all relative accuracy where tanh(inner) is within an ulp of
-# +-1 (|x| > ~4), because 1 + t and 1 - t^2 cancel; the error there is a few
-# ulps of 0.5 (1 + |t|) and of 0.5 |x| (1 + t^2) d_inner, and the argument's
-# rounding adds sech^2 times a few ulps of |inner|.  Likewise silu' near its
-# zero.  With fp32 exp and tanh good to about 2 ulps, 1e-5 leaves a margin of
-# about ten over the worst case.
+# formulas lose relative accuracy where tanh(inner) is within a few ulps of
+# +-1, because 1 + t and 1 - t^2 cancel; there the error is a few ulps of 1
+# in those differences (the floors below, in units of rel: 1e-6 for
+# 1 - t^2, 5e-7 for 1 + t, about eight and four ulps of 1), times the
+# factor they are multiplied by.  Where fp32 tanh is exactly +-1 both
+# differences are exact and the floors vanish, so saturated inputs are held
+# to the result itself.  Likewise silu' near its zero.  With fp32 exp and
+# tanh good to about 2 ulps, 1e-5 leaves a margin of about ten elsewhere.
 TOL = (1e-5, 1e-30)
+SECH2_FLOOR = 1e-6 / TOL[0]
+T_FLOOR = 5e-7 / TOL[0]

@@ -99,3 +99,30 @@ def test_gelu_inplace_streaming_without_copy():
     torch.cuda.synchronize()
     ry, sy = OA.gelu_inplace(c["gate"])
     cmp("gelu (no copy)", y.cpu(), ry, sy)
+
+
+def test_gelu_saturated_tails_exact():
+    """Where fp32 tanh is +-1 (|x| >= 9, |inner| >= 33), gelu' is exactly 1
+    or 0 ("ffn_gelu_backward ve ffn_swiglu_backward", "GeLU' (tanh
+    approximation)", with the input clamp of "WGSL-Spesifik Notlar" §2), so
+    grad_pre is exactly g or 0 and gelu(x) exactly x or 0: on the 16-byte
+    path and, through a view one float in, on the 4-byte path."""
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    mags = np.array([9.0, 20.0, 50.0, 100.0, 200.0, 1e30], np.float32)
+    x = np.concatenate([mags, -mags, np.resize(mags, 52), -np.resize(mags, 52)]).astype(np.float32)
+    g = np.random.default_rng(17).standard_normal(x.size).astype(np.float32) * np.float32(3.0)
+    want_d = np.where(x > 0, g, np.float32(0.0))
+    want_y = np.where(x > 0, x, np.float32(0.0))
+    for off in (0, 1):
+        # off = 1: the same values in a view starting one float into its buffer
+        gx = to_dev(np.concatenate([np.zeros(off, np.float32), g]))[off:]
+        xx = to_dev(np.concatenate([np.zeros(off, np.float32), x]))[off:]
+        n = x.size
+        say(f"gelu saturated tails, {'4-byte' if off else '16-byte'} path, n={n}")
+        dp = binding.ffn_gelu_backward(gx, xx)
+        y = xx.clone()
+        binding.gelu_inplace(y)
+        torch.cuda.synchronize()
+        assert np.array_equal(dp.cpu().numpy(), want_d), "grad_pre not exactly g or 0"
+        assert np.array_equal(y.cpu().numpy(), want_y), "gelu not exactly x or 0"
