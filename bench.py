@@ -16,8 +16,11 @@ before the timed region.  The value is TFLOP/s = 2*M*N*K summed over the step,
 divided by the wall time per step.  The roofline object describes the
 dominant kernel (lm_head) against the fp32 matrix-core peak of MI355X, with
 its average duration taken from HIP events that the launch itself records at
-the kernel's start and end (gemm_fwd_timed) for each of its launches in the
-timed region.  The per-kernel breakdown comes from a separate pass after the
+the kernel's start and end (gemm_opts.start_event / stop_event of the _ex
+entry points) for each of its launches in the timed region.  Every product
+goes through the _ex entry points with a workspace sized by
+gemm_fwd_workspace_bytes (only the SwiGLU down-projection splits K and uses
+it), allocated before the timed region.  The per-kernel breakdown comes from a separate pass after the
 timed region with such events on every launch.
 
 The CPU baseline is the fp64 oracle, timed on whole steps of the same five
@@ -664,12 +667,16 @@ def time_configs():
         N = W.shape[1]
         w16 = W.dtype == torch.float16
         Y = torch.empty((M, N), device=dev)
+        wsb = lib.gemm_fwd_workspace_bytes(M, K, N, int(swiglu), int(w16), -1)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+
         def launch(ev=(None, None)):
+            o = binding.opts(-1, ws.data_ptr() if wsb else None, wsb, *ev)
             if swiglu:
-                return lib.gemm_fwd_swiglu_timed(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(),
-                                                 Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
-            return lib.gemm_fwd_timed(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(),
-                                      Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+                return lib.gemm_fwd_swiglu_ex(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(),
+                                              Y.data_ptr(), M, K, N, int(w16), o, sp)
+            return lib.gemm_fwd_ex(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(),
+                                   Y.data_ptr(), M, K, N, int(w16), o, sp)
 
         def sample(n, flush_between):
             """n launches queued back to back (a flush kernel between them
@@ -776,12 +783,16 @@ def time_shards():
             Y = torch.empty((M, N), device=dev)
             R = d.get("R")
 
+            wsb = lib.gemm_fwd_workspace_bytes(M, K, N, int(swiglu), int(w16), -1)
+            ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+
             def launch(ev=(None, None)):
+                o = binding.opts(-1, ws.data_ptr() if wsb else None, wsb, *ev)
                 if swiglu:
-                    return lib.gemm_fwd_swiglu_timed(d["G"].data_ptr(), d["U"].data_ptr(), d["W"].data_ptr(),
-                                                     R.data_ptr(), Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
-                return lib.gemm_fwd_timed(d["X"].data_ptr(), d["W"].data_ptr(), None if R is None else R.data_ptr(),
-                                          Y.data_ptr(), M, K, N, int(w16), -1, sp, *ev)
+                    return lib.gemm_fwd_swiglu_ex(d["G"].data_ptr(), d["U"].data_ptr(), d["W"].data_ptr(),
+                                                  R.data_ptr(), Y.data_ptr(), M, K, N, int(w16), o, sp)
+                return lib.gemm_fwd_ex(d["X"].data_ptr(), d["W"].data_ptr(), None if R is None else R.data_ptr(),
+                                       Y.data_ptr(), M, K, N, int(w16), o, sp)
 
             t0 = time.perf_counter()
             while time.perf_counter() - t0 < 0.2:
@@ -862,23 +873,28 @@ def main():
         R = d(c["R"]) if "R" in c else None
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         w16 = c["W"].dtype == np.float16
+        lib = binding.load_library()
+        # split-K configurations take a workspace, allocated (zero-filled)
+        # here, outside the timed region
+        wsb = lib.gemm_fwd_workspace_bytes(M, K, N, int("G" in c), int(w16), -1)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
         if "G" in c:
             G, U = d(c["G"]), d(c["U"])
-            keep = (G, U, W, R, Y)
+            keep = (G, U, W, R, Y, ws)
             args_ = (G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(), Y.data_ptr(), M, K, N,
                      binding.GEMM_W_F16 if w16 else binding.GEMM_W_F32)
-            fn = binding.load_library().gemm_fwd_swiglu
-            timed = binding.load_library().gemm_fwd_swiglu_timed
+            fn = lib.gemm_fwd_swiglu_ex
             cfg = binding.kernel_config(M, K, N, swiglu=True, w16=w16)
         else:
             X = d(c["X"])
-            keep = (X, W, R, Y)
+            keep = (X, W, R, Y, ws)
             args_ = (X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), Y.data_ptr(), M, K, N,
                      binding.GEMM_FLAG_W_F16 if w16 else 0)
-            fn = binding.load_library().gemm_fwd
-            timed = binding.load_library().gemm_fwd_timed
+            fn = lib.gemm_fwd_ex
             cfg = binding.kernel_config(M, K, N, swiglu=False, w16=w16)
-        launches.append({"name": name, "fn": fn, "timed": timed, "args": args_, "keep": keep, "M": M, "K": K, "N": N,
+        plain = binding.opts(-1, ws.data_ptr() if wsb else None, wsb)
+        launches.append({"name": name, "fn": fn, "args": args_, "keep": keep, "M": M, "K": K, "N": N,
+                         "ws": (ws.data_ptr() if wsb else None, wsb), "plain": plain, "workspace_bytes": wsb,
                          "flops": 2 * M * N * K, "w16": w16, "config": cfg,
                          "bytes": (M * K * (8 if "G" in c else 4) + K * N * (2 if w16 else 4)
                                    + M * N * 4 * (2 if R is not None else 1))})
@@ -893,9 +909,9 @@ def main():
             if events is not None and i in which:
                 # the library records the pair at the kernel's own start and end
                 e0, e1 = events[i]
-                st = L["timed"](*L["args"], -1, sp, e0.cuda_event, e1.cuda_event)
+                st = L["fn"](*L["args"], binding.opts(-1, *L["ws"], e0.cuda_event, e1.cuda_event), sp)
             else:
-                st = L["fn"](*L["args"], sp)
+                st = L["fn"](*L["args"], L["plain"], sp)
             if st != 0:
                 raise RuntimeError(f"{L['name']}: {binding.status_string(st)}")
 
@@ -948,7 +964,7 @@ def main():
         avg_us = float(np.mean(ms)) * 1e3
         kernels[L["name"]] = {
             "M": L["M"], "K": L["K"], "N": L["N"], "w": "f16" if L["w16"] else "f32",
-            "config": L["config"], "avg_us": round(avg_us, 3),
+            "config": L["config"], "workspace_bytes": L["workspace_bytes"], "avg_us": round(avg_us, 3),
             "median_us": round(float(np.median(ms)) * 1e3, 3),
             "tflops": round(L["flops"] / avg_us / 1e6, 3),
             "frac_fp32_mfma_peak": round(L["flops"] / avg_us / 1e6 / PEAK_FP32_MFMA_TFLOPS, 4),

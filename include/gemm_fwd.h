@@ -36,29 +36,32 @@
  * outside the inputs is read.  Results are bitwise reproducible from run to
  * run for the same inputs, shape and configuration.
  *
- * Split-K workspace.  For small output grids with a long K (M * N <= 2^19)
- * the library may split K over several workgroups per output tile; their
- * fp32 partial tiles meet in a static device workspace that the library
- * holds for the life of the process (64 MiB plus 64 KiB of counters per
- * device), so no call allocates.  The workspace has 4 regions, and each
- * belongs to one stream: the first 4 distinct streams (by handle) that make
- * a split-K call each keep a region for the life of the process, and calls
- * on one stream, which run in order, share it (the four are counted over all
- * devices of the process, though each device has its own workspace).  Calls
- * on a later stream get no region: the library's own tile choice then takes
- * a configuration without split-K (same results within the tolerance, not
- * bit for bit), and
- * an explicit split-K configuration gives GEMM_ERR_CONFIG.  So split-K calls
- * on different streams never share workspace.  The special per-thread
- * default stream handle counts as a single stream: callers that use it from
- * several host threads at once must not rely on split-K configurations.  The
- * counters are left at zero by every call.
+ * State.  The library holds no mutable state and no device memory of its
+ * own: gemm_fwd and gemm_fwd_swiglu take nothing but the arrays, the shape
+ * and the stream, and every launch they make reads only the inputs and
+ * writes only Y.
+ *
+ * Workspace (the _ex entry points only).  For small output grids with a long
+ * K (e.g. M = 512, K = 3072, N = 768) the fastest configurations split K over
+ * two or more workgroups per output tile; their fp32 partial tiles meet in a
+ * workspace the caller provides (gemm_opts.workspace, device memory of
+ * gemm_opts.workspace_bytes bytes, 256-byte aligned, overlapping no array of
+ * the call).  gemm_fwd_workspace_bytes() gives the size a shape needs: a
+ * 64 KiB block of per-tile arrival counters (so a split-K configuration
+ * takes at most 16384 output tiles; more gives GEMM_ERR_CONFIG) followed by
+ * one M x N fp32 slot per split.  The workspace must be zero-filled before
+ * its first use; every call that completes leaves the counter block zero
+ * again (the slots keep partial tiles, which no later call reads before
+ * writing), so one zero-fill serves any number of calls of any shape.  Calls that share a workspace must not overlap in time
+ * (enqueue them on one stream, or order them with events); calls on
+ * different streams need different workspaces.  Without a workspace, or with
+ * one that is too small, the library's own choice takes a configuration that
+ * does not split K (the same function within the tolerance, not bit for
+ * bit); an explicit split-K configuration then gives GEMM_ERR_WORKSPACE.
  *
  * Errors.  Arguments are validated synchronously before anything is enqueued;
  * on a negative status nothing is launched and Y is untouched.  No exception or
- * abort crosses this interface.  Calls may be made from several host threads;
- * the only mutable host state is the mutex-guarded table that assigns the
- * workspace regions to streams.
+ * abort crosses this interface.  Calls may be made from several host threads.
  *
  * Preconditions (the page's host-side rule that K and N be multiples of 4 for
  * the 16-byte vector loads, "Önemli Optimizasyonlar" §1):
@@ -86,8 +89,10 @@ extern "C" {
 #define GEMM_ERR_DTYPE (-4)  /* unknown flag bits or w_dtype */
 #define GEMM_ERR_ALIAS (-5)  /* Y overlaps an input */
 #define GEMM_ERR_LAUNCH (-6) /* the HIP runtime reported an error at launch */
-#define GEMM_ERR_CONFIG (-7) /* an explicit tile configuration index is out of range, or it splits K and
-                                the shape exceeds the workspace or the stream has no workspace region */
+#define GEMM_ERR_CONFIG (-7) /* a tile configuration index is out of range */
+#define GEMM_ERR_WORKSPACE (-8) /* an explicit split-K configuration without a large enough workspace, or a
+                                   workspace pointer and size that do not match (NULL with a nonzero size,
+                                   or a negative size) */
 
 /* gemm_fwd flags. */
 #define GEMM_FLAG_W_F16 0x1u /* W holds IEEE binary16 values; otherwise fp32 */
@@ -117,32 +122,44 @@ int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const flo
                     int64_t M, int64_t K, int64_t N, int w_dtype, void *stream);
 
 /*
- * Same operations with an explicit tile configuration (config >= 0, an index
- * below gemm_num_configs()), or the library's own choice (config < 0).  Every
- * configuration computes the same function; they differ in tile shape and
- * speed, and results may differ in the last bits between configurations.
- * Used by tuning sweeps and by tests that cover every kernel instantiation.
+ * Options of the _ex entry points.  Every field has a neutral value: a NULL
+ * gemm_opts pointer, or one with config = -1 and everything else 0/NULL,
+ * makes an _ex call exactly the plain one.
+ *   config          -1: the library's choice; otherwise an index below
+ *                   gemm_num_configs() (gemm_bwd_num_configs() for the
+ *                   backward products).  Every configuration computes the
+ *                   same function; they differ in tile shape and speed, and
+ *                   results may differ in the last bits between them.
+ *   workspace       device memory for split-K partial tiles, or NULL (see
+ *   workspace_bytes "Workspace" above); 256-byte aligned.
+ *   start_event     hipEvent_t handles created by the caller, or NULL: the
+ *   stop_event      kernel's own start and end are recorded into them, so
+ *                   hipEventElapsedTime(start, stop) is the kernel's run time
+ *                   without the stream's dispatch latency.  Nothing is
+ *                   recorded when the status is negative or when there is
+ *                   nothing to launch (an empty output).
+ * An out-of-range config gives GEMM_ERR_CONFIG.
  */
-int gemm_fwd_cfg(const float *X, const void *W, const float *R, float *Y,
-                 int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream);
-int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
-                        int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream);
+typedef struct gemm_opts {
+    int64_t config;
+    void *workspace;
+    int64_t workspace_bytes;
+    void *start_event;
+    void *stop_event;
+} gemm_opts;
+
+int gemm_fwd_ex(const float *X, const void *W, const float *R, float *Y,
+                int64_t M, int64_t K, int64_t N, uint32_t flags, const gemm_opts *opts, void *stream);
+int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                       int64_t M, int64_t K, int64_t N, int w_dtype, const gemm_opts *opts, void *stream);
 
 /*
- * Same as gemm_fwd_cfg / gemm_fwd_swiglu_cfg, and in addition the kernel's own
- * start and end are recorded into `start` and `stop` (hipEvent_t handles
- * created by the caller; either may be NULL).  Unlike hipEventRecord calls
- * placed around an ordinary launch, these exclude the stream's dispatch
- * latency, so hipEventElapsedTime(start, stop) is the kernel's run time.  For
- * timing harnesses; nothing is recorded when the status is negative or when
- * there is nothing to launch (M == 0 or N == 0).
+ * Bytes of workspace a forward call needs: for `config` (>= 0), or for the
+ * library's choice when a workspace is given (config = -1); 0 when that
+ * configuration does not split K.  swiglu is 0/1, flags as for gemm_fwd.
+ * Returns -1 for bad arguments.
  */
-int gemm_fwd_timed(const float *X, const void *W, const float *R, float *Y,
-                   int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream,
-                   void *start, void *stop);
-int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
-                          int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream,
-                          void *start, void *stop);
+int64_t gemm_fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int swiglu, uint32_t flags, int config);
 
 /* Backward-product flags. */
 #define GEMM_FLAG_ACC 0x2u /* add the product to the output's current contents (the *_acc kernels) */
@@ -171,8 +188,8 @@ int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, con
  * N % 4 == 0; M (the contraction of matmul_at) is unrestricted; limits as
  * for gemm_fwd.  An empty output enqueues nothing; an empty contraction
  * writes zeros (or leaves the output unchanged with GEMM_FLAG_ACC).  Flags
- * other than GEMM_FLAG_ACC give GEMM_ERR_DTYPE.  The split-K workspace rules
- * of gemm_fwd apply.  Returns GEMM_OK or a negative status, validated before
+ * other than GEMM_FLAG_ACC give GEMM_ERR_DTYPE.  The workspace rules of
+ * gemm_fwd_ex apply to the _ex forms below.  Returns GEMM_OK or a negative status, validated before
  * anything is enqueued.
  */
 int gemm_matmul_t(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
@@ -200,24 +217,32 @@ int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY,
  */
 int gemm_matmul_t_swiglu_bwd(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
                              float *dUP, int64_t M, int64_t K, int64_t N, void *stream);
-int gemm_matmul_t_swiglu_bwd_cfg(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
-                                 float *dUP, int64_t M, int64_t K, int64_t N, int config, void *stream);
 
-/* The same with an explicit configuration of the backward table (config >= 0,
- * below gemm_bwd_num_configs()), or the library's choice (config < 0). */
-int gemm_matmul_t_cfg(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
-                      int config, void *stream);
-int gemm_matmul_at_cfg(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
-                       int config, void *stream);
-int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
-                                int64_t K, int64_t N, uint32_t flags, int config, void *stream);
+/* The backward products with options (gemm_opts above; config indexes the
+ * backward table, below gemm_bwd_num_configs()).  The lm_head's input
+ * gradient (M = 512, K = 768, N = 16384) splits its long contraction over
+ * workgroups when a workspace is given. */
+int gemm_matmul_t_ex(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                     const gemm_opts *opts, void *stream);
+int gemm_matmul_at_ex(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                      const gemm_opts *opts, void *stream);
+int gemm_matmul_at_swiglu_a_ex(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
+                               int64_t K, int64_t N, uint32_t flags, const gemm_opts *opts, void *stream);
+int gemm_matmul_t_swiglu_bwd_ex(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                                float *dUP, int64_t M, int64_t K, int64_t N, const gemm_opts *opts, void *stream);
+
+/* Bytes of workspace a backward call needs (op 1: matmul_t, 2: matmul_at;
+ * M, K, N and swiglu as in the calls above; config as for
+ * gemm_fwd_workspace_bytes); -1 for bad arguments. */
+int64_t gemm_bwd_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int swiglu, int config);
 
 /* Number and static names of the backward products' configurations, and the
  * one the library picks for a shape (op 1: matmul_t, 2: matmul_at; M, K, N
- * and swiglu as in the calls above; -1 for an unknown op). */
+ * and swiglu as in the calls above; with_workspace 0/1: whether the call has
+ * a large enough workspace; -1 for an unknown op). */
 int gemm_bwd_num_configs(void);
 const char *gemm_bwd_config_name(int config);
-int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu);
+int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, int with_workspace);
 
 /* Number of tile configurations compiled into the library. */
 int gemm_num_configs(void);
@@ -225,10 +250,10 @@ int gemm_num_configs(void);
 /* Static name of a configuration ("BMxBNxBK_..."), or NULL if out of range. */
 const char *gemm_config_name(int config);
 
-/* The configuration the library picks for a shape (swiglu, w_f16 are 0/1),
- * on a stream that holds a split-K workspace region (a stream without one
- * gets the choice without split-K instead). */
-int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16);
+/* The configuration the library picks for a shape (swiglu, w_f16 and
+ * with_workspace are 0/1; with_workspace: whether the call has a large enough
+ * workspace). */
+int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16, int with_workspace);
 
 /* Static text for a status code. */
 const char *gemm_status_string(int status);

@@ -63,7 +63,7 @@ def test_probe_library_exports_its_header():
 
 def test_status_codes_match_header(lib):
     for name in ["GEMM_OK", "GEMM_ERR_NULL", "GEMM_ERR_SHAPE", "GEMM_ERR_ALIGN", "GEMM_ERR_DTYPE",
-                 "GEMM_ERR_ALIAS", "GEMM_ERR_LAUNCH", "GEMM_ERR_CONFIG"]:
+                 "GEMM_ERR_ALIAS", "GEMM_ERR_LAUNCH", "GEMM_ERR_CONFIG", "GEMM_ERR_WORKSPACE"]:
         code = _status(name)
         text = lib.gemm_status_string(code).decode()
         assert text and text != "unknown status", name
@@ -81,18 +81,22 @@ def test_config_table(lib):
                   (512, 3072, 768), (256, 4096, 768), (512, 768, 768), (8192, 768, 50304), (1, 4, 4)]:
         for sw in (0, 1):
             for w16 in (0, 1):
-                assert 0 <= lib.gemm_select_config(*shape, sw, w16) < n
+                for ws in (0, 1):
+                    assert 0 <= lib.gemm_select_config(*shape, sw, w16, ws) < n
 
-    def pick(M, K, N, sw, w16):
-        return lib.gemm_config_name(lib.gemm_select_config(M, K, N, sw, w16)).decode()
+    def pick(M, K, N, sw, w16, ws=1):
+        return lib.gemm_config_name(lib.gemm_select_config(M, K, N, sw, w16, ws)).decode()
     # the workload configurations (their tiles are the ones bench.py times)
     assert pick(128, 768, 768, 0, 0) == "16x48x128_k4_sp4_dAW"
     assert pick(512, 768, 768, 0, 0) == "32x48x64_k4_sp4_pf3_dAW"
-    assert pick(512, 3072, 768, 1, 0) == "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
+    assert pick(512, 3072, 768, 1, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
     assert pick(512, 768, 16384, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert pick(512, 768, 3072, 0, 1) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert pick(8192, 3072, 768, 1, 1) == "64x384x32_w1x4_sp8_pf4_il"
     assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    # without a workspace the long-K small grid does not split K
+    assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x64_k4_sp8_pf3_il"
+    assert pick(512, 3072, 768, 0, 0) == "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
     # mid-size grids: 128 x 64 while it gives two tiles per CU, 64 x 64 when
     # it fills one whole round and 64 x 48 does not
     assert pick(512, 768, 8192, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
@@ -102,16 +106,49 @@ def test_config_table(lib):
     assert pick(8192, 3072, 768, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
 
 
+def test_workspace_sizes(lib):
+    """gemm_fwd_workspace_bytes / gemm_bwd_workspace_bytes: 0 for the
+    configurations that do not split K; otherwise the 64 KiB counter block
+    plus one M x N fp32 slot per split."""
+    names = [lib.gemm_config_name(i).decode() for i in range(lib.gemm_num_configs())]
+    CNT = 64 << 10
+    # 512 x 3072 x 768 SwiGLU: 32 x 96 tiles, K split in two
+    assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 1, 0, -1) == CNT + 2 * 512 * 768 * 4
+    assert lib.gemm_fwd_workspace_bytes(512, 768, 16384, 0, 1, -1) == 0
+    assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 1, 0, names.index("128x128x32_w2x2_sp4_pf3_il_dA")) == 0
+    ks8 = names.index("128x96x64_w2x2_sp8_ks8")
+    assert lib.gemm_fwd_workspace_bytes(100, 64, 200, 0, 0, ks8) == CNT + 8 * 100 * 200 * 4
+    # more output tiles than the counter block holds: refused
+    assert lib.gemm_fwd_workspace_bytes(128 * 200, 64, 96 * 100, 0, 0, ks8) == -1
+    assert lib.gemm_fwd_workspace_bytes(0, 64, 64, 0, 0, -1) == 0
+    assert lib.gemm_fwd_workspace_bytes(-1, 64, 64, 0, 0, -1) == -1
+    assert lib.gemm_fwd_workspace_bytes(64, 64, 64, 0, 2, -1) == -1
+    assert lib.gemm_fwd_workspace_bytes(64, 64, 64, 0, 0, len(names)) == -1
+    # the lm_head's input gradient: 128 x 96 tiles with the 16384-long
+    # contraction split eight ways
+    assert lib.gemm_bwd_workspace_bytes(1, 512, 768, 16384, 0, -1) == CNT + 8 * 512 * 768 * 4
+    assert lib.gemm_bwd_workspace_bytes(2, 512, 768, 16384, 0, -1) == 0
+    assert lib.gemm_bwd_workspace_bytes(3, 512, 768, 16384, 0, -1) == -1
+
+
 # fake, well-aligned, non-overlapping host addresses
 X, W, R, Y, U = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 
 
-def fwd(lib, x=X, w=W, r=R, y=Y, M=64, K=64, N=64, flags=0, config=-1):
-    return lib.gemm_fwd_cfg(x, w, r, y, M, K, N, flags, config, None)
+WS = 0x60000000  # a fake workspace
 
 
-def sw(lib, g=X, u=U, w=W, r=R, y=Y, M=64, K=64, N=64, wd=0, config=-1):
-    return lib.gemm_fwd_swiglu_cfg(g, u, w, r, y, M, K, N, wd, config, None)
+def _opts(config=-1, ws=None, wsb=0):
+    from tiled_dense_gemm_matmul_amd import binding
+    return binding.opts(config, ws, wsb)
+
+
+def fwd(lib, x=X, w=W, r=R, y=Y, M=64, K=64, N=64, flags=0, config=-1, ws=None, wsb=0):
+    return lib.gemm_fwd_ex(x, w, r, y, M, K, N, flags, _opts(config, ws, wsb), None)
+
+
+def sw(lib, g=X, u=U, w=W, r=R, y=Y, M=64, K=64, N=64, wd=0, config=-1, ws=None, wsb=0):
+    return lib.gemm_fwd_swiglu_ex(g, u, w, r, y, M, K, N, wd, _opts(config, ws, wsb), None)
 
 
 def test_null_pointers(lib):
@@ -158,6 +195,35 @@ def test_dtype_and_config(lib):
     assert sw(lib, wd=2) == _status("GEMM_ERR_DTYPE")
     assert sw(lib, wd=-1) == _status("GEMM_ERR_DTYPE")
     assert fwd(lib, config=lib.gemm_num_configs()) == _status("GEMM_ERR_CONFIG")
+    assert fwd(lib, config=-2) == _status("GEMM_ERR_CONFIG")
+
+
+def test_workspace_validation(lib):
+    """The workspace is checked before anything is enqueued: a split-K
+    configuration forced without one, or with one that is too small, a
+    pointer/size mismatch, a misaligned or overlapping workspace."""
+    WSE, ALIGN, ALIAS = _status("GEMM_ERR_WORKSPACE"), _status("GEMM_ERR_ALIGN"), _status("GEMM_ERR_ALIAS")
+    names = [lib.gemm_config_name(i).decode() for i in range(lib.gemm_num_configs())]
+    ks2 = names.index("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW")
+    need = lib.gemm_fwd_workspace_bytes(64, 256, 64, 1, 0, ks2)
+    assert need > 0
+    assert sw(lib, K=256, config=ks2) == WSE
+    assert sw(lib, K=256, config=ks2, ws=WS, wsb=need - 1) == WSE
+    assert sw(lib, K=256, ws=None, wsb=64) == WSE
+    assert sw(lib, K=256, ws=WS, wsb=-1) == WSE
+    assert sw(lib, K=256, config=ks2, ws=WS + 16, wsb=need) == ALIGN
+    assert sw(lib, K=256, config=ks2, ws=Y - 256, wsb=need) == ALIAS
+    assert sw(lib, K=256, config=ks2, ws=X + 256, wsb=need) == ALIAS
+    # a workspace adjacent to the arrays passes validation (checked on a
+    # no-op shape)
+    assert sw(lib, M=0, K=256, config=ks2, ws=WS, wsb=need) == _status("GEMM_OK")
+    # backward: the same rules
+    at = names  # (unused; the backward table has its own names)
+    del at
+    bwd = [lib.gemm_bwd_config_name(i).decode() for i in range(lib.gemm_bwd_num_configs())]
+    ks8 = bwd.index("128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA")
+    t = lambda c=-1, ws=None, wsb=0: lib.gemm_matmul_t_ex(X, W, Y, 64, 64, 256, 0, _opts(c, ws, wsb), None)
+    assert t(c=ks8) == WSE and t(ws=None, wsb=8) == WSE and t(c=ks8, ws=WS + 128, wsb=1 << 20) == ALIGN
 
 
 def test_alias(lib):
@@ -193,10 +259,12 @@ def test_backward_validation(lib):
     NULL, SHAPE, ALIGN = _status("GEMM_ERR_NULL"), _status("GEMM_ERR_SHAPE"), _status("GEMM_ERR_ALIGN")
     DTYPE, ALIAS, CONFIG = _status("GEMM_ERR_DTYPE"), _status("GEMM_ERR_ALIAS"), _status("GEMM_ERR_CONFIG")
     ACC = 0x2
-    t = lambda dy=X, w=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_t_cfg(dy, w, y, M, K, N, f, c, None)
-    at = lambda x=X, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_cfg(x, dy, y, M, K, N, f, c, None)
-    ats = lambda g=X, u=U, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_swiglu_a_cfg(
-        g, u, dy, y, M, K, N, f, c, None)
+    t = lambda dy=X, w=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_t_ex(dy, w, y, M, K, N, f, _opts(c),
+                                                                                   None)
+    at = lambda x=X, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_ex(x, dy, y, M, K, N, f, _opts(c),
+                                                                                    None)
+    ats = lambda g=X, u=U, dy=W, y=Y, M=64, K=64, N=64, f=0, c=-1: lib.gemm_matmul_at_swiglu_a_ex(
+        g, u, dy, y, M, K, N, f, _opts(c), None)
     assert t(dy=None) == NULL and t(w=None) == NULL and t(y=None) == NULL
     assert at(x=None) == NULL and at(dy=None) == NULL and ats(u=None) == NULL
     assert t(K=6) == SHAPE and t(N=6) == SHAPE and at(K=10) == SHAPE and t(M=-1) == SHAPE
@@ -213,17 +281,19 @@ def test_backward_validation(lib):
 
 def test_backward_selection(lib):
     n = lib.gemm_bwd_num_configs()
-    lib.gemm_bwd_select_config.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
     for op in (1, 2):
         for shape in [(512, 768, 768), (512, 3072, 768), (512, 768, 3072), (512, 768, 16384), (8192, 3072, 768),
                       (1, 4, 4)]:
             for sw in ((0, 1) if op == 2 else (0,)):
-                assert 0 <= lib.gemm_bwd_select_config(op, *shape, sw) < n, (op, shape, sw)
-    assert lib.gemm_bwd_select_config(0, 512, 768, 768, 0) == -1
-    assert lib.gemm_bwd_select_config(3, 512, 768, 768, 0) == -1
+                for ws in (0, 1):
+                    assert 0 <= lib.gemm_bwd_select_config(op, *shape, sw, ws) < n, (op, shape, sw, ws)
+    assert lib.gemm_bwd_select_config(0, 512, 768, 768, 0, 1) == -1
+    assert lib.gemm_bwd_select_config(3, 512, 768, 768, 0, 1) == -1
 
-    def name(op, *shape):
-        return lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(op, *shape, 0)).decode()
+    def name(op, *shape, ws=1):
+        return lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(op, *shape, 0, ws)).decode()
+    # without a workspace the lm_head's input gradient does not split K
+    assert name(1, 512, 768, 16384, ws=0) == "16x96x64_k4_sp8_pf3_il"
     # dW of the 768 x 768 projections: 384 tiles of 32 x 48 would take two
     # rounds on 256 CUs, 256 tiles of 48 x 48 take one
     assert name(2, 512, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
@@ -240,9 +310,9 @@ def test_backward_selection(lib):
     assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
     assert name(2, 8192, 768, 3072) == "48x48x64_k4_sp4_pf3_dAW"
     assert name(2, 8192, 1024, 4096) == "32x48x64_k4_sp4_pf3_dAW"
-    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1)).decode() == \
+    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1, 1)).decode() == \
         "96x96x64_w2x2_sp4_pf3_il_dA"
-    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1)).decode() == \
+    assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1, 1)).decode() == \
         "32x48x64_k4_sp4_pf3_dAW"
 
 

@@ -21,12 +21,25 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmfwd
 _lib = None
 
 EXPORTED = (
-    "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_cfg", "gemm_fwd_swiglu_cfg",
+    "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_ex", "gemm_fwd_swiglu_ex", "gemm_fwd_workspace_bytes",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
-    "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_cfg", "gemm_matmul_at_cfg",
-    "gemm_matmul_at_swiglu_a_cfg", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
-    "gemm_matmul_t_swiglu_bwd", "gemm_matmul_t_swiglu_bwd_cfg", "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward", "act_gelu_inplace",
+    "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_ex", "gemm_matmul_at_ex",
+    "gemm_matmul_at_swiglu_a_ex", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
+    "gemm_bwd_workspace_bytes", "gemm_matmul_t_swiglu_bwd", "gemm_matmul_t_swiglu_bwd_ex",
+    "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward",
+    "act_gelu_inplace",
 )
+
+
+class GemmOpts(ctypes.Structure):
+    """struct gemm_opts of include/gemm_fwd.h."""
+    _fields_ = [("config", ctypes.c_int64), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
+
+
+def opts(config=-1, workspace=None, workspace_bytes=0, start=None, stop=None):
+    """A gemm_opts passed by reference (ctypes.byref) to the _ex entry points."""
+    return ctypes.byref(GemmOpts(-1 if config is None else int(config), workspace, int(workspace_bytes), start, stop))
 
 
 class GemmError(RuntimeError):
@@ -53,36 +66,37 @@ def load_library():
     lib.gemm_fwd.restype = c_int
     lib.gemm_fwd_swiglu.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, p]
     lib.gemm_fwd_swiglu.restype = c_int
-    lib.gemm_fwd_cfg.argtypes = [p, p, p, p, i64, i64, i64, u32, c_int, p]
-    lib.gemm_fwd_cfg.restype = c_int
-    lib.gemm_fwd_swiglu_cfg.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, c_int, p]
-    lib.gemm_fwd_swiglu_cfg.restype = c_int
-    lib.gemm_fwd_timed.argtypes = [p, p, p, p, i64, i64, i64, u32, c_int, p, p, p]
-    lib.gemm_fwd_timed.restype = c_int
-    lib.gemm_fwd_swiglu_timed.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, c_int, p, p, p]
-    lib.gemm_fwd_swiglu_timed.restype = c_int
+    o = ctypes.c_void_p  # const gemm_opts * (ctypes.byref or None)
+    lib.gemm_fwd_ex.argtypes = [p, p, p, p, i64, i64, i64, u32, o, p]
+    lib.gemm_fwd_ex.restype = c_int
+    lib.gemm_fwd_swiglu_ex.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, o, p]
+    lib.gemm_fwd_swiglu_ex.restype = c_int
+    lib.gemm_fwd_workspace_bytes.argtypes = [i64, i64, i64, c_int, u32, c_int]
+    lib.gemm_fwd_workspace_bytes.restype = i64
     lib.gemm_num_configs.argtypes = []
     lib.gemm_num_configs.restype = c_int
     lib.gemm_config_name.argtypes = [c_int]
     lib.gemm_config_name.restype = ctypes.c_char_p
-    lib.gemm_select_config.argtypes = [i64, i64, i64, c_int, c_int]
+    lib.gemm_select_config.argtypes = [i64, i64, i64, c_int, c_int, c_int]
     lib.gemm_select_config.restype = c_int
     lib.gemm_status_string.argtypes = [c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
     for name, n_in in (("gemm_matmul_t", 2), ("gemm_matmul_at", 2), ("gemm_matmul_at_swiglu_a", 3)):
         getattr(lib, name).argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, p]
         getattr(lib, name).restype = c_int
-        getattr(lib, name + "_cfg").argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, c_int, p]
-        getattr(lib, name + "_cfg").restype = c_int
+        getattr(lib, name + "_ex").argtypes = [p] * (n_in + 1) + [i64, i64, i64, u32, o, p]
+        getattr(lib, name + "_ex").restype = c_int
     lib.gemm_matmul_t_swiglu_bwd.argtypes = [p] * 6 + [i64, i64, i64, p]
     lib.gemm_matmul_t_swiglu_bwd.restype = c_int
-    lib.gemm_matmul_t_swiglu_bwd_cfg.argtypes = [p] * 6 + [i64, i64, i64, c_int, p]
-    lib.gemm_matmul_t_swiglu_bwd_cfg.restype = c_int
+    lib.gemm_matmul_t_swiglu_bwd_ex.argtypes = [p] * 6 + [i64, i64, i64, o, p]
+    lib.gemm_matmul_t_swiglu_bwd_ex.restype = c_int
+    lib.gemm_bwd_workspace_bytes.argtypes = [c_int, i64, i64, i64, c_int, c_int]
+    lib.gemm_bwd_workspace_bytes.restype = i64
     lib.gemm_bwd_num_configs.argtypes = []
     lib.gemm_bwd_num_configs.restype = c_int
     lib.gemm_bwd_config_name.argtypes = [c_int]
     lib.gemm_bwd_config_name.restype = ctypes.c_char_p
-    lib.gemm_bwd_select_config.argtypes = [c_int, i64, i64, i64, c_int]
+    lib.gemm_bwd_select_config.argtypes = [c_int, i64, i64, i64, c_int, c_int]
     lib.gemm_bwd_select_config.restype = c_int
     f32 = ctypes.c_float
     lib.loss_cross_entropy.argtypes = [p, p, p, i64, i64, f32, f32, f32, p]
@@ -121,32 +135,71 @@ def bwd_config_name(config: int):
     return None if name is None else name.decode()
 
 
-def bwd_kernel_config(op, M, K, N, swiglu=False) -> str:
+def bwd_kernel_config(op, M, K, N, swiglu=False, workspace=True) -> str:
     """Name of the configuration the library picks for a backward product
-    (op "matmul_t" or "matmul_at"; M, K, N the forward's names)."""
+    (op "matmul_t" or "matmul_at"; M, K, N the forward's names), with or
+    without a workspace."""
     code = {"matmul_t": 1, "matmul_at": 2}[op]
-    return bwd_config_name(load_library().gemm_bwd_select_config(code, M, K, N, int(swiglu)))
+    return bwd_config_name(load_library().gemm_bwd_select_config(code, M, K, N, int(swiglu), int(workspace)))
 
 
-def kernel_config(M, K, N, swiglu=False, w16=False) -> str:
-    """Name of the tile configuration the library picks for a shape."""
-    return config_name(load_library().gemm_select_config(M, K, N, int(swiglu), int(w16)))
+def kernel_config(M, K, N, swiglu=False, w16=False, workspace=True) -> str:
+    """Name of the tile configuration the library picks for a shape, with or
+    without a workspace."""
+    return config_name(load_library().gemm_select_config(M, K, N, int(swiglu), int(w16), int(workspace)))
+
+
+# --- split-K workspaces ---
+#
+# The library holds no device memory: split-K partial tiles go to a
+# workspace the caller provides.  The tensor-level calls below keep one
+# zero-filled torch buffer per (device, stream), grown on demand; the library
+# leaves a workspace zeroed after every call, and calls on one stream are
+# ordered, so the buffer is reused as it is.  Calls on different streams get
+# different buffers.
+
+_workspaces = {}
+
+
+def workspace(device, stream, nbytes):
+    """(pointer, size) of the zero-filled workspace for `stream` on `device`,
+    at least nbytes long; (None, 0) when nbytes is 0."""
+    if nbytes <= 0:
+        return None, 0
+    key = (device.index, int(stream.cuda_stream))
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            # rounded up to a MiB: a few sizes serve every shape
+            buf = torch.zeros(((nbytes + (1 << 20) - 1) >> 20) << 20, dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def _fwd_workspace(M, K, N, swiglu, w16, device, config):
+    nbytes = load_library().gemm_fwd_workspace_bytes(M, K, N, int(swiglu), GEMM_FLAG_W_F16 if w16 else 0,
+                                                     -1 if config is None else int(config))
+    if nbytes < 0:
+        raise GemmError(-2, "gemm_fwd_workspace_bytes")
+    return workspace(device, torch.cuda.current_stream(device), nbytes)
 
 
 # --- raw pointer-level calls (same names and argument order as the C ABI) ---
 
-def gemm_fwd(X, W, R, Y, M, K, N, flags, stream, config=-1) -> int:
-    lib = load_library()
-    if config is None or config < 0:
-        return lib.gemm_fwd(X, W, R, Y, M, K, N, flags, stream)
-    return lib.gemm_fwd_cfg(X, W, R, Y, M, K, N, flags, config, stream)
+def gemm_fwd(X, W, R, Y, M, K, N, flags, stream) -> int:
+    return load_library().gemm_fwd(X, W, R, Y, M, K, N, flags, stream)
 
 
-def gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream, config=-1) -> int:
-    lib = load_library()
-    if config is None or config < 0:
-        return lib.gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream)
-    return lib.gemm_fwd_swiglu_cfg(G, U, W, R, Y, M, K, N, w_dtype, config, stream)
+def gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream) -> int:
+    return load_library().gemm_fwd_swiglu(G, U, W, R, Y, M, K, N, w_dtype, stream)
+
+
+def gemm_fwd_ex(X, W, R, Y, M, K, N, flags, options, stream) -> int:
+    return load_library().gemm_fwd_ex(X, W, R, Y, M, K, N, flags, options, stream)
+
+
+def gemm_fwd_swiglu_ex(G, U, W, R, Y, M, K, N, w_dtype, options, stream) -> int:
+    return load_library().gemm_fwd_swiglu_ex(G, U, W, R, Y, M, K, N, w_dtype, options, stream)
 
 
 # --- tensor-level API ---
@@ -182,8 +235,11 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def matmul(X, W, R=None, out=None, config=None):
-    """Y = X @ W (+ R).  X [M, K] f32, W [K, N] f32 or f16, R [M, N] f32 or None."""
+def matmul(X, W, R=None, out=None, config=None, use_workspace=True):
+    """Y = X @ W (+ R).  X [M, K] f32, W [K, N] f32 or f16, R [M, N] f32 or None.
+    config: a configuration index (None: the library's choice).  use_workspace:
+    give the library the stream's split-K workspace (False: the plain
+    gemm_fwd behaviour, no split-K)."""
     if not isinstance(X, torch.Tensor) or X.dim() != 2:
         raise TypeError("X must be a 2-D torch.Tensor [M, K]")
     M, K = X.shape
@@ -196,23 +252,26 @@ def matmul(X, W, R=None, out=None, config=None):
         out = torch.empty((M, N), dtype=torch.float32, device=device)
     else:
         _check_act(out, "out", (M, N), device)
-    flags = GEMM_FLAG_W_F16 if W.dtype == torch.float16 else 0
-    st = gemm_fwd(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), out.data_ptr(),
-                  M, K, N, flags, _stream(device), -1 if config is None else config)
+    w16 = W.dtype == torch.float16
+    flags = GEMM_FLAG_W_F16 if w16 else 0
+    ws, wsb = _fwd_workspace(M, K, N, False, w16, device, config) if use_workspace else (None, 0)
+    st = gemm_fwd_ex(X.data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), out.data_ptr(),
+                     M, K, N, flags, opts(config, ws, wsb), _stream(device))
     if st != 0:
-        raise GemmError(st, "gemm_fwd")
+        raise GemmError(st, "gemm_fwd_ex")
     return out
 
 
-def matmul_residual(X, W, R, out=None, config=None):
+def matmul_residual(X, W, R, out=None, config=None, use_workspace=True):
     """Y = X @ W + R."""
     if R is None:
         raise ValueError("matmul_residual needs R")
-    return matmul(X, W, R, out=out, config=config)
+    return matmul(X, W, R, out=out, config=config, use_workspace=use_workspace)
 
 
-def matmul_residual_swiglu_a(G, U, W, R, out=None, config=None):
-    """Y = (silu(G) * U) @ W + R, the SwiGLU combine fused into the A load."""
+def matmul_residual_swiglu_a(G, U, W, R, out=None, config=None, use_workspace=True):
+    """Y = (silu(G) * U) @ W + R, the SwiGLU combine fused into the A load
+    (config and use_workspace as for matmul)."""
     if not isinstance(G, torch.Tensor) or G.dim() != 2:
         raise TypeError("G must be a 2-D torch.Tensor [M, K]")
     M, K = G.shape
@@ -225,23 +284,32 @@ def matmul_residual_swiglu_a(G, U, W, R, out=None, config=None):
         out = torch.empty((M, N), dtype=torch.float32, device=device)
     else:
         _check_act(out, "out", (M, N), device)
-    w_dtype = GEMM_W_F16 if W.dtype == torch.float16 else GEMM_W_F32
-    st = gemm_fwd_swiglu(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(),
-                         M, K, N, w_dtype, _stream(device), -1 if config is None else config)
+    w16 = W.dtype == torch.float16
+    w_dtype = GEMM_W_F16 if w16 else GEMM_W_F32
+    ws, wsb = _fwd_workspace(M, K, N, True, w16, device, config) if use_workspace else (None, 0)
+    st = gemm_fwd_swiglu_ex(G.data_ptr(), U.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(),
+                            M, K, N, w_dtype, opts(config, ws, wsb), _stream(device))
     if st != 0:
-        raise GemmError(st, "gemm_fwd_swiglu")
+        raise GemmError(st, "gemm_fwd_swiglu_ex")
     return out
 
 
 # --- backward linear family (matmul_t, matmul_at and their _acc / _swiglu_a forms) ---
 
-def _bwd_call(name, ptrs, M, K, N, acc, device, config):
+def _bwd_workspace(op, M, K, N, swiglu, device, config):
+    nbytes = load_library().gemm_bwd_workspace_bytes(op, M, K, N, int(swiglu), -1 if config is None else int(config))
+    if nbytes < 0:
+        raise GemmError(-2, "gemm_bwd_workspace_bytes")
+    return workspace(device, torch.cuda.current_stream(device), nbytes)
+
+
+def _bwd_call(name, ptrs, M, K, N, acc, device, config, use_workspace=True):
     lib = load_library()
     flags = GEMM_FLAG_ACC if acc else 0
-    if config is None or config < 0:
-        st = getattr(lib, name)(*ptrs, M, K, N, flags, _stream(device))
-    else:
-        st = getattr(lib, name + "_cfg")(*ptrs, M, K, N, flags, int(config), _stream(device))
+    op = 1 if name == "gemm_matmul_t" else 2
+    ws, wsb = (_bwd_workspace(op, M, K, N, name.endswith("swiglu_a"), device, config) if use_workspace
+               else (None, 0))
+    st = getattr(lib, name + "_ex")(*ptrs, M, K, N, flags, opts(config, ws, wsb), _stream(device))
     if st != 0:
         raise GemmError(st, name)
 
@@ -255,7 +323,7 @@ def _out(out, shape, device, acc):
     return out
 
 
-def matmul_t(dY, W, out=None, acc=False, config=None):
+def matmul_t(dY, W, out=None, acc=False, config=None, use_workspace=True):
     """dX = dY @ W^T (matmul_t), or out += dY @ W^T with acc=True (matmul_t_acc).
     dY [M, N] f32, W [K, N] f32 (the forward's weight); dX [M, K]."""
     if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
@@ -268,11 +336,12 @@ def matmul_t(dY, W, out=None, acc=False, config=None):
     K = W.shape[0]
     _check_act(W, "W", (K, N), device)
     out = _out(out, (M, K), device, acc)
-    _bwd_call("gemm_matmul_t", (dY.data_ptr(), W.data_ptr(), out.data_ptr()), M, K, N, acc, device, config)
+    _bwd_call("gemm_matmul_t", (dY.data_ptr(), W.data_ptr(), out.data_ptr()), M, K, N, acc, device, config,
+              use_workspace)
     return out
 
 
-def matmul_at(X, dY, out=None, acc=False, config=None):
+def matmul_at(X, dY, out=None, acc=False, config=None, use_workspace=True):
     """dW = X^T @ dY (matmul_at), or out += X^T @ dY with acc=True (matmul_at_acc).
     X [M, K] f32, dY [M, N] f32; dW [K, N]."""
     if not isinstance(X, torch.Tensor) or X.dim() != 2:
@@ -285,11 +354,12 @@ def matmul_at(X, dY, out=None, acc=False, config=None):
     N = dY.shape[1]
     _check_act(dY, "dY", (M, N), device)
     out = _out(out, (K, N), device, acc)
-    _bwd_call("gemm_matmul_at", (X.data_ptr(), dY.data_ptr(), out.data_ptr()), M, K, N, acc, device, config)
+    _bwd_call("gemm_matmul_at", (X.data_ptr(), dY.data_ptr(), out.data_ptr()), M, K, N, acc, device, config,
+              use_workspace)
     return out
 
 
-def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None):
+def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None, use_workspace=True):
     """dW = (silu(G) * U)^T @ dY (matmul_at_swiglu_a), or out += ... with acc=True
     (matmul_at_acc_swiglu_a); the combine is recomputed as A is staged.
     G, U [M, K] f32, dY [M, N] f32; dW [K, N]."""
@@ -305,7 +375,7 @@ def matmul_at_swiglu_a(G, U, dY, out=None, acc=False, config=None):
     _check_act(dY, "dY", (M, N), device)
     out = _out(out, (K, N), device, acc)
     _bwd_call("gemm_matmul_at_swiglu_a", (G.data_ptr(), U.data_ptr(), dY.data_ptr(), out.data_ptr()),
-              M, K, N, acc, device, config)
+              M, K, N, acc, device, config, use_workspace)
     return out
 
 
@@ -332,12 +402,10 @@ def matmul_t_swiglu_backward(dY, W, G, U, grad_gate=None, grad_up=None, config=N
     _check_act(grad_up, "grad_up", (M, K), device)
     lib = load_library()
     ptrs = (dY.data_ptr(), W.data_ptr(), G.data_ptr(), U.data_ptr(), grad_gate.data_ptr(), grad_up.data_ptr())
-    if config is None or config < 0:
-        st = lib.gemm_matmul_t_swiglu_bwd(*ptrs, M, K, N, _stream(device))
-    else:
-        st = lib.gemm_matmul_t_swiglu_bwd_cfg(*ptrs, M, K, N, int(config), _stream(device))
+    ws, wsb = _bwd_workspace(1, M, K, N, False, device, config)
+    st = lib.gemm_matmul_t_swiglu_bwd_ex(*ptrs, M, K, N, opts(config, ws, wsb), _stream(device))
     if st != 0:
-        raise GemmError(st, "gemm_matmul_t_swiglu_bwd")
+        raise GemmError(st, "gemm_matmul_t_swiglu_bwd_ex")
     return grad_gate, grad_up
 
 

@@ -51,7 +51,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "gemm_fwd.h"
@@ -75,23 +74,21 @@ struct Params {
     int tiles_m, tiles_n;
     int group_m;     // M-tiles per group in the tile order
     int kchunk;      // K range of one split (a multiple of BK) when K is split
-    int region;      // split-K workspace region of this call
+    // split-K only (KS > 1), in the caller's workspace: KS partial tiles per
+    // output tile (split s writes its partial of output element (i, j) at
+    // ws[s * ws_stride + i * N + j]) and one arrival counter per output tile,
+    // zero between calls
+    float *ws;
+    unsigned *cnt;
+    int64_t ws_stride;
 };
 
-// Split-K workspace.  When a configuration splits K over KS workgroups per
-// output tile, each writes its fp32 partial tile into its own slot, then
-// bumps the tile's counter; the last to arrive adds the KS slots in the fixed
-// order 0..KS-1 (so results do not depend on arrival order), adds R, writes
-// Y and resets the counter.  Static storage, zero at load, so no call
-// allocates.  The kSkRegions regions belong to streams (stream_region):
-// calls on one stream run in order and share their stream's region, and
-// calls on different streams never share one.
-constexpr int kSkRegions = 4;
+// Split-K.  When a configuration splits K over KS workgroups per output
+// tile, each writes its fp32 partial tile into its own slot of the caller's
+// workspace, then bumps the tile's counter; the last to arrive adds the KS
+// slots in the fixed order 0..KS-1 (so results do not depend on arrival
+// order), adds R, writes Y and resets the counter to zero.
 constexpr int kSkMaxSplit = 8;
-constexpr int kSkMaxElems = 1 << 19;   // M * N limit for split-K calls
-constexpr int kSkMaxTiles = 4096;
-__device__ float g_sk_ws[kSkRegions][kSkMaxSplit][kSkMaxElems];
-__device__ unsigned g_sk_cnt[kSkRegions][kSkMaxTiles];
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -851,10 +848,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         // Publish this split's partial tile, then count the arrival.
         __shared__ int sk_last;
         const int tile_id = tm * p.tiles_n + tn;
-        float *const slot0 = &g_sk_ws[p.region][0][0];
+        // the tile's valid rows span rows_valid * N elements of a slot
+        const int pbytes = rows_valid * N * 4;
         if (computes) {
-            const Rsrc rP = make_rsrc(slot0 + (size_t)split * kSkMaxElems + tile_off,
-                                      (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
+            const Rsrc rP = make_rsrc(p.ws + split * p.ws_stride + tile_off, pbytes);
 #pragma unroll
             for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
                 const int idx = tid + it * NC;
@@ -876,12 +873,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0)
-            sk_last = __hip_atomic_fetch_add(&g_sk_cnt[p.region][tile_id], 1u, __ATOMIC_RELAXED,
+            sk_last = __hip_atomic_fetch_add(p.cnt + tile_id, 1u, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(KS - 1);
         __syncthreads();
         if (!sk_last || !computes) return;
         if (tid == 0)
-            __hip_atomic_store(&g_sk_cnt[p.region][tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int ybytes = rows_valid * N * 4;
         const auto finish = make_finish(ybytes);
 #pragma unroll
@@ -903,9 +900,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 if (sp == split) {
                     v += own;
                 } else {
-                    const Rsrc rP = make_rsrc(slot0 + (size_t)sp * kSkMaxElems + tile_off,
-                                              (int)(((int64_t)kSkMaxElems - (int64_t)tile_off) * 4));
-                    v += load_f32x4_coherent(rP, off);
+                    v += load_f32x4_coherent(make_rsrc(p.ws + sp * p.ws_stride + tile_off, pbytes), off);
                 }
             }
             finish(v, off);
@@ -960,59 +955,32 @@ constexpr ConfigEntry make_entry(const char *name) {
                          {gemm_fwd_kernel<C, true, true, false>, gemm_fwd_kernel<C, true, true, true>}}}};
 }
 
-// Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL>: the configurations
-// that win on some shape of the forward family, plus one of each kind of
-// pipeline so that every code path stays built and tested.
+// Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL, PRIO, DMA>: the
+// tiles the library's own choice takes (select_config), then one of each
+// other kind of pipeline, so that every code path stays built and tested.
 const ConfigEntry kConfigs[] = {
-    // specialised: NP staging waves beside the compute waves
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 1>>("128x128x32_w2x2_sp4_cil"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 8, 2, 1>>("128x128x32_w2x2_sp8"),
-    make_entry<Tile<128, 256, 32, 2, 2, 1, 4, 2, 1>>("128x256x32_w2x2_sp4"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 3, 1, 1>>("128x192x32_w2x2_sp8_pf3_il"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 2, 1>>("128x192x32_w2x2_sp8"),
-    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1>>("64x64x64_w2x2_sp4"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 4, 2, 1>>("64x96x64_w2x2_sp4"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1>>("64x48x64_w2x1_k2_sp8_pf3"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1>>("64x48x64_w2x1_k2_sp4_pf3_il"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1>>("32x48x64_k4_sp4_pf3"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1>>("32x48x64_k4_sp4_pf3_cil"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1>>("16x48x128_k4_sp4"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
-    // specialised with the K range split over KS workgroups
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 1, 2, 1>>("32x96x64_w1x2_k2_sp8_pf4_il_ks2_cil"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 4, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf4_ks2_cil_dW"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 0, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_ks2_cil_dW"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_il_dA"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_dA"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 0, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_dA"),
-    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 2, 1, 0, 1, 0, 2, 3>>("64x48x64_w2x1_k2_sp4_pf2_dAW"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 0, 1, 0, 2, 2>>("16x96x64_k4_sp8_pf3_dW"),
-    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 0, 4, 1, 2, 2>>("32x192x64_w1x4_sp8_pf3_ks4_cil_dW"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 0, 4, 1, 2, 2>>("64x96x64_w2x2_sp8_pf3_ks4_cil_dW"),
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 0, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_dA"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 1, 2, 2>>("32x48x64_k4_sp4_pf3_cil_dW"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
-    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
-    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<64, 384, 32, 1, 4, 1, 8, 4, 1, 1>>("64x384x32_w1x4_sp8_pf4_il"),
+    make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
-    make_entry<Tile<32, 192, 64, 1, 4, 1, 8, 3, 1, 1, 4>>("32x192x64_w1x4_sp8_pf3_il_ks4"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 8, 3, 1, 1, 4, 1>>("64x96x64_w2x2_sp8_pf3_il_ks4_cil"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("32x48x64_k4_sp8_pf3_il_ks2"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1, 2>>("16x96x64_k4_sp8_pf3_il_ks2"),
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
+    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
+    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
+    make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    // specialised, register staging only, two stages of loads in flight
+    make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
+    // specialised, three stages in flight without the interleaving hint,
+    // eight staging waves
+    make_entry<Tile<64, 48, 64, 2, 1, 2, 8, 3, 1>>("64x48x64_w2x1_k2_sp8_pf3"),
+    // K split over eight workgroups
     make_entry<Tile<128, 96, 64, 2, 2, 1, 8, 2, 1, 0, 8>>("128x96x64_w2x2_sp8_ks8"),
-    // cooperative: every wave stages and computes
-    make_entry<Tile<128, 128, 32, 2, 2, 1, 0, 1, 2>>("128x128x32_w2x2"),
+    // cooperative: every wave stages and computes (one, then two stages of
+    // loads in flight)
     make_entry<Tile<64, 64, 64, 2, 2, 1, 0, 1, 2>>("64x64x64_w2x2"),
-    make_entry<Tile<64, 96, 64, 2, 2, 1, 0, 2, 1>>("64x96x64_w2x2_pf2"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 0, 2, 2>>("32x48x64_k4_pf2"),
-    make_entry<Tile<16, 48, 128, 1, 1, 4, 0, 2, 2>>("16x48x128_k4_pf2"),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1055,27 +1023,26 @@ constexpr int kNumBwdConfigs = sizeof(kBwdConfigs) / sizeof(kBwdConfigs[0]);
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Split-K calls use the static workspace: the whole M x N output must fit a
-// slot and every tile needs a counter.
-bool split_fits(const ConfigEntry &e, int64_t M, int64_t N) {
-    return M * N <= kSkMaxElems && ceil_div(M, e.bm) * ceil_div(N, e.bn) <= kSkMaxTiles;
-}
+// The library's own choice splits K over workgroups only for outputs of at
+// most this many elements: the range where it was measured to win (larger
+// outputs fill the CUs without it, e.g. the 8192-token weight gradients).
+constexpr int64_t kSplitMaxElems = (int64_t)1 << 19;
 
-// Split-K workspace regions, one per stream: each of the first kSkRegions
-// distinct streams that make a split-K call keeps a region for the life of
-// the process (calls on one stream run in order, so they can share it).
-// Returns -1 when every region belongs to another stream.
-std::mutex g_region_mu;
-void *g_region_owner[kSkRegions];
-int g_regions_taken = 0;
+// Workspace layout: a fixed block of kCounterBytes holding one arrival
+// counter per output tile (so a call never finds another call's partial
+// tiles where its counters are: only the counters are left zero after a
+// call), then KS partial slots of M x N floats.
+constexpr int64_t kCounterBytes = 64 << 10;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
 
-int stream_region(void *stream) {
-    std::lock_guard<std::mutex> lock(g_region_mu);
-    for (int r = 0; r < g_regions_taken; ++r)
-        if (g_region_owner[r] == stream) return r;
-    if (g_regions_taken == kSkRegions) return -1;
-    g_region_owner[g_regions_taken] = stream;
-    return g_regions_taken++;
+// Bytes a split-K configuration needs for an M x N output; zero for a
+// configuration without split-K, -1 for one with more output tiles than the
+// counter block holds.
+int64_t split_workspace_bytes(const ConfigEntry &e, int64_t M, int64_t N) {
+    if (e.ks <= 1) return 0;
+    const int64_t tiles = ceil_div(M, e.bm) * ceil_div(N, e.bn);
+    if (tiles > kMaxSplitTiles) return -1;
+    return kCounterBytes + (int64_t)e.ks * M * N * 4;
 }
 
 int table_index(const ConfigEntry *table, int count, const char *name) {
@@ -1101,10 +1068,12 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // than 128 x 192 on the shapes measured.  And 64 x 64 tiles
 // rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
 // and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
-// `split` false: only configurations without split-K (for a stream that has
-// no workspace region).  `forward` false: the rule as the backward products
-// measured it, without the 128 x 64 tile and the whole-round 64 x 64 choice.
-int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split = true, bool forward = true) {
+// Long K on a small grid splits K over two workgroups when the caller
+// provides a workspace (`split`); the forward SwiGLU product then stages
+// 128-deep slices of K (512 x 3072 x 768: 26.5 against 26.9 us with 64).
+// `forward` false: the rule as the backward products measured it, without
+// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep split.
+int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward = true) {
     (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
     static const int swiglu_wide = config_index("64x384x32_w1x4_sp8_pf4_il");
@@ -1115,11 +1084,13 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
     static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
+    static const int deep_split128 = config_index("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int tiny = config_index("16x48x128_k4_sp4_dAW");
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
     static const bool complete = big >= 0 && swiglu_wide >= 0 && wide >= 0 && tall >= 0 && mid >= 0 &&
-                                 narrow >= 0 && small >= 0 && deep >= 0 && deep_split >= 0 && tiny >= 0;
+                                 narrow >= 0 && small >= 0 && deep >= 0 && deep_split >= 0 &&
+                                 deep_split128 >= 0 && tiny >= 0;
     if (!complete) return -1;
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
@@ -1134,9 +1105,10 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     if (t48 >= cus) return narrow;
     if (M <= 128) return tiny;
     if (K >= 2048) {
-        // long K on a small grid: split K in two when the workspace holds it
-        if (split && split_fits(kConfigs[deep_split], M, N) && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
-            return deep_split;
+        // long K on a small grid: split K in two when there is a workspace
+        // (for outputs up to 2^19 elements, the range measured)
+        if (split && M * N <= kSplitMaxElems && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
+            return forward && swiglu ? deep_split128 : deep_split;
         return deep;
     }
     return small;
@@ -1156,18 +1128,17 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // transposed A come to between one and two per CU while 48 x 48 tiles come
 // to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
 // at 768 x 512 x 768, and 98 against over 125 us for the 16 x 96 tiles the
-// forward rule picks at 768 x 8192 x 768 (whose output is too large for the
-// split-K workspace).  A transposed B takes 128 x 64 tiles where they come to
-// two per CU and 128 x 128 tiles do not: 74 against 80 us at 8192 x 768 x 768
-// and 282 against over 300 at 8192 x 3072 x 768.  The SwiGLU weight gradient
-// over a contraction of 4096 or more takes 96 x 96 tiles where they fill the
-// CUs, combining G and U half as often: 346 against 364 us at
-// 3072 x 8192 x 768.  Other weight gradients over a contraction of 4096 or
-// more take 48 x 48 tiles too where the output splits into whole ones:
-// 311 against 331 us at 3072 x 8192 x 768, 610 against 638 at
-// 768 x 16384 x 3072 (with ragged 48-row tiles, 1024 x 8192 x 4096, they
-// lose 3%).
-int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split = true) {
+// forward rule picks at 768 x 8192 x 768.  A transposed B takes 128 x 64
+// tiles where they come to two per CU and 128 x 128 tiles do not: 74 against
+// 80 us at 8192 x 768 x 768 and 282 against over 300 at 8192 x 3072 x 768.
+// The SwiGLU weight gradient over a contraction of 4096 or more takes
+// 96 x 96 tiles where they fill the CUs, combining G and U half as often:
+// 346 against 364 us at 3072 x 8192 x 768.  Other weight gradients over a
+// contraction of 4096 or more take 48 x 48 tiles too where the output splits
+// into whole ones: 311 against 331 us at 3072 x 8192 x 768, 610 against 638
+// at 768 x 16384 x 3072 (with ragged 48-row tiles, 1024 x 8192 x 4096, they
+// lose 3%).  The split-K tiles need the caller's workspace (`split`).
+int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
     static const int fwd_mid = config_index("64x64x64_w2x2_sp4_dAW");
     static const int mid = table_index(kBwdConfigs, kNumBwdConfigs, "64x64x64_w2x2_sp4");
     static const int fwd_deep = config_index("16x96x64_k4_sp8_pf3_il");
@@ -1188,7 +1159,7 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     // without split-K the forward rule's long-K choice is the deep tile
     const bool long_k_grid = f == fwd_deep_split || (!split && f == fwd_deep);
     if (op == kOpNT && long_k_grid && K <= 4096) return tiny;
-    if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && split_fits(kBwdConfigs[long_k], M, N) &&
+    if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && M * N <= kSplitMaxElems &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
         return long_k;
     // a transposed A takes 32 x 48 tiles where the forward rule takes 64 x 64
@@ -1218,9 +1189,55 @@ bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Options of the _ex entry points, with the plain entry points' defaults.
+struct Opts {
+    int config = -1;
+    void *ws = nullptr;
+    int64_t ws_bytes = 0;
+    void *start = nullptr, *stop = nullptr;
+};
+
+int read_opts(const gemm_opts *o, int num_configs, Opts &out) {
+    if (o == nullptr) return GEMM_OK;
+    if (o->config < -1 || o->config >= num_configs) return GEMM_ERR_CONFIG;
+    if (o->workspace_bytes < 0 || (o->workspace == nullptr && o->workspace_bytes != 0)) return GEMM_ERR_WORKSPACE;
+    if (o->workspace != nullptr && !aligned(o->workspace, 256)) return GEMM_ERR_ALIGN;
+    out.config = (int)o->config;
+    out.ws = o->workspace;
+    out.ws_bytes = o->workspace_bytes;
+    out.start = o->start_event;
+    out.stop = o->stop_event;
+    return GEMM_OK;
+}
+
+// The configuration to launch: the explicit one, or the library's choice,
+// which splits K only when the workspace holds what that needs.  Fills the
+// split-K fields of p.
+template <class Pick>
+int resolve(const ConfigEntry *table, const Opts &o, int64_t M, int64_t N, Pick pick, Params &p, int &cfg) {
+    cfg = o.config >= 0 ? o.config : pick(o.ws != nullptr);
+    if (cfg < 0) return GEMM_ERR_CONFIG;
+    int64_t need = split_workspace_bytes(table[cfg], M, N);
+    if (need < 0) return GEMM_ERR_CONFIG;
+    if (need > o.ws_bytes) {
+        if (o.config >= 0) return GEMM_ERR_WORKSPACE;
+        cfg = pick(false);
+        if (cfg < 0) return GEMM_ERR_CONFIG;
+        need = split_workspace_bytes(table[cfg], M, N);
+        if (need != 0) return GEMM_ERR_CONFIG;
+    }
+    p.ws = nullptr;
+    p.cnt = nullptr;
+    p.ws_stride = M * N;
+    if (need > 0) {
+        p.cnt = static_cast<unsigned *>(o.ws);
+        p.ws = reinterpret_cast<float *>(static_cast<char *>(o.ws) + kCounterBytes);
+    }
+    return GEMM_OK;
+}
+
 int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, const float *R, float *Y,
-        int64_t M, int64_t K, int64_t N, int config, void *stream, void *start = nullptr,
-        void *stop = nullptr) {
+        int64_t M, int64_t K, int64_t N, const Opts &o, void *stream) {
     const int64_t lim = (int64_t)1 << 31;
     if (M < 0 || K < 0 || N < 0 || M >= lim || K >= lim || N >= lim) return GEMM_ERR_SHAPE;
     // A pointer may be NULL only when its array holds no element (an empty
@@ -1234,7 +1251,6 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     // stage's rows of W and a tile's rows of Y (up to 256 x N fp32) must each
     // stay below 2^31 bytes.
     if (K * 1024 >= lim || N * 1024 >= lim) return GEMM_ERR_SHAPE;
-    if (config >= kNumConfigs) return GEMM_ERR_CONFIG;
     if ((A && !aligned(A, 16)) || (Y && !aligned(Y, 16)) || (U && !aligned(U, 16)) || (R && !aligned(R, 16)) ||
         (W && !aligned(W, w16 ? 8 : 16)))
         return GEMM_ERR_ALIGN;
@@ -1243,28 +1259,26 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     if (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, U, abytes) ||
         overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, R, ybytes))
         return GEMM_ERR_ALIAS;
+    const size_t wsb = (size_t)o.ws_bytes;
+    if (overlaps(o.ws, wsb, Y, ybytes) || overlaps(o.ws, wsb, A, abytes) || overlaps(o.ws, wsb, U, abytes) ||
+        overlaps(o.ws, wsb, W, wbytes) || overlaps(o.ws, wsb, R, ybytes))
+        return GEMM_ERR_ALIAS;
     if (M == 0 || N == 0) return GEMM_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0) {
         const int64_t count = M * N;
         hipExtLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s,
-                              static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop), 0, R, Y, count);
+                              static_cast<hipEvent_t>(o.start), static_cast<hipEvent_t>(o.stop), 0, R, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
 
-    int cfg = config >= 0 ? config : select_config(M, K, N, swiglu, w16);
-    if (cfg < 0 || cfg >= kNumConfigs) return GEMM_ERR_CONFIG;
-    int region = 0;
-    if (kConfigs[cfg].ks > 1) {
-        if (!split_fits(kConfigs[cfg], M, N)) return GEMM_ERR_CONFIG;
-        region = stream_region(stream);
-        if (region < 0 && config >= 0) return GEMM_ERR_CONFIG;
-        if (region < 0) cfg = select_config(M, K, N, swiglu, w16, false);
-        if (cfg < 0) return GEMM_ERR_CONFIG;
-    }
-    const ConfigEntry &e = kConfigs[cfg];
     Params p;
+    int cfg = -1;
+    const int st = resolve(kConfigs, o, M, N,
+                           [&](bool split) { return select_config(M, K, N, swiglu, w16, split); }, p, cfg);
+    if (st != GEMM_OK) return st;
+    const ConfigEntry &e = kConfigs[cfg];
     p.A = A; p.U = U; p.W = W; p.R = R; p.Y = Y;
     p.EG = nullptr; p.EU = nullptr; p.Y2 = nullptr;
     p.M = (int)M; p.K = (int)K; p.N = (int)N;
@@ -1272,14 +1286,13 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     p.tiles_n = (int)ceil_div(N, e.bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     p.kchunk = (int)(ceil_div(ceil_div(K, e.ks), e.bk) * e.bk);
-    p.region = region;
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
     // with NULL events this is a plain launch; otherwise the events take the
     // kernel's own start and end times
-    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, static_cast<hipEvent_t>(start),
-                          static_cast<hipEvent_t>(stop), 0, p);
+    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, static_cast<hipEvent_t>(o.start),
+                          static_cast<hipEvent_t>(o.stop), 0, p);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -1290,7 +1303,7 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
 // with A = X, or silu(GATE) * UP.  `acc` adds the product to the output's
 // current contents.
 int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B, float *Y, int64_t M,
-            int64_t K, int64_t N, bool acc, int config, void *stream, const float *EG = nullptr,
+            int64_t K, int64_t N, bool acc, const Opts &o, void *stream, const float *EG = nullptr,
             const float *EU = nullptr, float *Y2 = nullptr) {
     // op kOpNT with swiglu: the fused SwiGLU backward, dGATE into Y and dUP
     // into Y2 from GATE (EG) and UP (EU), all [M x K]
@@ -1306,7 +1319,6 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
     if (fused && acc) return GEMM_ERR_DTYPE;
     if (K % 4 != 0 || N % 4 != 0) return GEMM_ERR_SHAPE;
     if (K * 1024 >= lim || N * 1024 >= lim) return GEMM_ERR_SHAPE;
-    if (config >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
     if ((A && !aligned(A, 16)) || (U && !aligned(U, 16)) || (B && !aligned(B, 16)) || (Y && !aligned(Y, 16)) ||
         (EG && !aligned(EG, 16)) || (EU && !aligned(EU, 16)) || (Y2 && !aligned(Y2, 16)))
         return GEMM_ERR_ALIGN;
@@ -1318,40 +1330,43 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
     if (fused) {
         // each output may be GATE's or UP's very array (every element is read
         // before it is written, by one thread) but overlaps nothing else
-        auto partial = [&](const void *o, const void *i) { return o != i && overlaps(o, ybytes, i, ybytes); };
+        auto partial = [&](const void *o2, const void *i) { return o2 != i && overlaps(o2, ybytes, i, ybytes); };
         if (overlaps(Y2, ybytes, A, abytes) || overlaps(Y2, ybytes, B, bbytes) || overlaps(Y, ybytes, Y2, ybytes) ||
             partial(Y, EG) || partial(Y, EU) || partial(Y2, EG) || partial(Y2, EU))
             return GEMM_ERR_ALIAS;
     }
+    const size_t wsb = (size_t)o.ws_bytes;
+    if (overlaps(o.ws, wsb, Y, ybytes) || overlaps(o.ws, wsb, A, abytes) || overlaps(o.ws, wsb, U, abytes) ||
+        overlaps(o.ws, wsb, B, bbytes) || (fused && (overlaps(o.ws, wsb, Y2, ybytes) ||
+                                                     overlaps(o.ws, wsb, EG, ybytes) || overlaps(o.ws, wsb, EU, ybytes))))
+        return GEMM_ERR_ALIAS;
     // kernel dimensions: output rows, contraction, output columns
     const int64_t km = op == kOpNT ? M : K, kk = op == kOpNT ? N : M, kn2 = op == kOpNT ? K : N;
     if (km == 0 || kn2 == 0) return GEMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(o.start), e1 = static_cast<hipEvent_t>(o.stop);
     if (kk == 0 && fused) {
         // dH = 0: both gradients are zero
-        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, nullptr, Y, km * kn2);
-        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, nullptr, Y2,
-                           km * kn2);
+        hipExtLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, e0,
+                              nullptr, 0, nullptr, Y, km * kn2);
+        hipExtLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(km * kn2, 256)), dim3(256), 0, s, nullptr,
+                              e1, 0, nullptr, Y2, km * kn2);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     if (kk == 0) {
         if (acc) return GEMM_OK;  // nothing to add
         const int64_t count = km * kn2;
-        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, nullptr, Y, count);
+        hipExtLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, e0, e1, 0,
+                              nullptr, Y, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
-    int cfg = config >= 0 ? config : select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu);
-    if (cfg < 0 || cfg >= kNumBwdConfigs) return GEMM_ERR_CONFIG;
-    int region = 0;
-    if (kBwdConfigs[cfg].ks > 1) {
-        if (!split_fits(kBwdConfigs[cfg], km, kn2)) return GEMM_ERR_CONFIG;
-        region = stream_region(stream);
-        if (region < 0 && config >= 0) return GEMM_ERR_CONFIG;
-        if (region < 0) cfg = select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu, false);
-        if (cfg < 0) return GEMM_ERR_CONFIG;
-    }
-    const ConfigEntry &e = kBwdConfigs[cfg];
     Params p;
+    int cfg = -1;
+    const int st = resolve(kBwdConfigs, o, km, kn2,
+                           [&](bool split) { return select_bwd_config(op, km, kk, kn2, fused ? 0 : swiglu, split); },
+                           p, cfg);
+    if (st != GEMM_OK) return st;
+    const ConfigEntry &e = kBwdConfigs[cfg];
     p.A = A; p.U = U; p.W = B; p.R = acc ? Y : nullptr; p.Y = Y;
     p.EG = EG; p.EU = EU; p.Y2 = Y2;
     p.M = (int)km; p.K = (int)kk; p.N = (int)kn2;
@@ -1359,95 +1374,128 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
     p.tiles_n = (int)ceil_div(kn2, e.bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     p.kchunk = (int)(ceil_div(ceil_div(kk, e.ks), e.bk) * e.bk);
-    p.region = region;
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[op == kOpTN ? 1 : 0][swiglu ? 1 : 0][acc ? 1 : 0];
     if (fn == nullptr) return GEMM_ERR_DTYPE;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, p);
+    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, e0, e1, 0, p);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int fwd_flags(uint32_t flags, bool &w16) {
+    if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
+    w16 = (flags & GEMM_FLAG_W_F16) != 0;
+    return GEMM_OK;
+}
+
+int bwd_flags(uint32_t flags, bool &acc) {
+    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
+    acc = (flags & GEMM_FLAG_ACC) != 0;
+    return GEMM_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-int gemm_fwd_cfg(const float *X, const void *W, const float *R, float *Y,
-                 int64_t M, int64_t K, int64_t N, uint32_t flags, int config, void *stream) {
-    if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
-    return run(false, X, nullptr, W, (flags & GEMM_FLAG_W_F16) != 0, R, Y, M, K, N, config, stream);
+int gemm_fwd_ex(const float *X, const void *W, const float *R, float *Y, int64_t M, int64_t K, int64_t N,
+                uint32_t flags, const gemm_opts *opts, void *stream) {
+    bool w16 = false;
+    Opts o;
+    int st = fwd_flags(flags, w16);
+    if (st == GEMM_OK) st = read_opts(opts, kNumConfigs, o);
+    return st != GEMM_OK ? st : run(false, X, nullptr, W, w16, R, Y, M, K, N, o, stream);
 }
 
-int gemm_fwd(const float *X, const void *W, const float *R, float *Y,
-             int64_t M, int64_t K, int64_t N, uint32_t flags, void *stream) {
-    return gemm_fwd_cfg(X, W, R, Y, M, K, N, flags, -1, stream);
-}
-int gemm_fwd_timed(const float *X, const void *W, const float *R, float *Y, int64_t M, int64_t K, int64_t N,
-                   uint32_t flags, int config, void *stream, void *start, void *stop) {
-    if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
-    return run(false, X, nullptr, W, (flags & GEMM_FLAG_W_F16) != 0, R, Y, M, K, N, config, stream, start,
-               stop);
+int gemm_fwd(const float *X, const void *W, const float *R, float *Y, int64_t M, int64_t K, int64_t N,
+             uint32_t flags, void *stream) {
+    return gemm_fwd_ex(X, W, R, Y, M, K, N, flags, nullptr, stream);
 }
 
-int gemm_fwd_swiglu_cfg(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
-                        int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream) {
+int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const float *R, float *Y, int64_t M,
+                       int64_t K, int64_t N, int w_dtype, const gemm_opts *opts, void *stream) {
     if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
-    return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, config, stream);
+    Opts o;
+    const int st = read_opts(opts, kNumConfigs, o);
+    return st != GEMM_OK ? st : run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, o, stream);
 }
 
-int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
-                    int64_t M, int64_t K, int64_t N, int w_dtype, void *stream) {
-    return gemm_fwd_swiglu_cfg(GATE, UP, W, R, Y, M, K, N, w_dtype, -1, stream);
-}
-int gemm_fwd_swiglu_timed(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
-                          int64_t M, int64_t K, int64_t N, int w_dtype, int config, void *stream, void *start,
-                          void *stop) {
-    if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
-    return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, config, stream, start, stop);
+int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y, int64_t M,
+                    int64_t K, int64_t N, int w_dtype, void *stream) {
+    return gemm_fwd_swiglu_ex(GATE, UP, W, R, Y, M, K, N, w_dtype, nullptr, stream);
 }
 
-int gemm_matmul_t_cfg(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
-                      int config, void *stream) {
-    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
-    return run_bwd(kOpNT, false, dY, nullptr, W, dX, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+int64_t gemm_fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int swiglu, uint32_t flags, int config) {
+    bool w16 = false;
+    if (fwd_flags(flags, w16) != GEMM_OK || M < 0 || K < 0 || N < 0 || config < -1 || config >= kNumConfigs)
+        return -1;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    const int cfg = config >= 0 ? config : select_config(M, K, N, swiglu != 0, w16, true);
+    return cfg < 0 ? -1 : split_workspace_bytes(kConfigs[cfg], M, N);
+}
+
+int gemm_matmul_t_ex(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                     const gemm_opts *opts, void *stream) {
+    bool acc = false;
+    Opts o;
+    int st = bwd_flags(flags, acc);
+    if (st == GEMM_OK) st = read_opts(opts, kNumBwdConfigs, o);
+    return st != GEMM_OK ? st : run_bwd(kOpNT, false, dY, nullptr, W, dX, M, K, N, acc, o, stream);
 }
 int gemm_matmul_t(const float *dY, const float *W, float *dX, int64_t M, int64_t K, int64_t N, uint32_t flags,
                   void *stream) {
-    return gemm_matmul_t_cfg(dY, W, dX, M, K, N, flags, -1, stream);
+    return gemm_matmul_t_ex(dY, W, dX, M, K, N, flags, nullptr, stream);
 }
-int gemm_matmul_at_cfg(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
-                       int config, void *stream) {
-    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
-    return run_bwd(kOpTN, false, X, nullptr, dY, dW, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+int gemm_matmul_at_ex(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
+                      const gemm_opts *opts, void *stream) {
+    bool acc = false;
+    Opts o;
+    int st = bwd_flags(flags, acc);
+    if (st == GEMM_OK) st = read_opts(opts, kNumBwdConfigs, o);
+    return st != GEMM_OK ? st : run_bwd(kOpTN, false, X, nullptr, dY, dW, M, K, N, acc, o, stream);
 }
 int gemm_matmul_at(const float *X, const float *dY, float *dW, int64_t M, int64_t K, int64_t N, uint32_t flags,
                    void *stream) {
-    return gemm_matmul_at_cfg(X, dY, dW, M, K, N, flags, -1, stream);
+    return gemm_matmul_at_ex(X, dY, dW, M, K, N, flags, nullptr, stream);
 }
-int gemm_matmul_at_swiglu_a_cfg(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
-                                int64_t K, int64_t N, uint32_t flags, int config, void *stream) {
-    if (flags & ~GEMM_FLAG_ACC) return GEMM_ERR_DTYPE;
-    return run_bwd(kOpTN, true, GATE, UP, dY, dW, M, K, N, (flags & GEMM_FLAG_ACC) != 0, config, stream);
+int gemm_matmul_at_swiglu_a_ex(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M,
+                               int64_t K, int64_t N, uint32_t flags, const gemm_opts *opts, void *stream) {
+    bool acc = false;
+    Opts o;
+    int st = bwd_flags(flags, acc);
+    if (st == GEMM_OK) st = read_opts(opts, kNumBwdConfigs, o);
+    return st != GEMM_OK ? st : run_bwd(kOpTN, true, GATE, UP, dY, dW, M, K, N, acc, o, stream);
 }
 int gemm_matmul_at_swiglu_a(const float *GATE, const float *UP, const float *dY, float *dW, int64_t M, int64_t K,
                             int64_t N, uint32_t flags, void *stream) {
-    return gemm_matmul_at_swiglu_a_cfg(GATE, UP, dY, dW, M, K, N, flags, -1, stream);
+    return gemm_matmul_at_swiglu_a_ex(GATE, UP, dY, dW, M, K, N, flags, nullptr, stream);
 }
-
-int gemm_matmul_t_swiglu_bwd_cfg(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
-                                 float *dUP, int64_t M, int64_t K, int64_t N, int config, void *stream) {
-    return run_bwd(kOpNT, true, dY, nullptr, W, dGATE, M, K, N, false, config, stream, GATE, UP, dUP);
+int gemm_matmul_t_swiglu_bwd_ex(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
+                                float *dUP, int64_t M, int64_t K, int64_t N, const gemm_opts *opts, void *stream) {
+    Opts o;
+    const int st = read_opts(opts, kNumBwdConfigs, o);
+    return st != GEMM_OK ? st : run_bwd(kOpNT, true, dY, nullptr, W, dGATE, M, K, N, false, o, stream, GATE, UP, dUP);
 }
 int gemm_matmul_t_swiglu_bwd(const float *dY, const float *W, const float *GATE, const float *UP, float *dGATE,
                              float *dUP, int64_t M, int64_t K, int64_t N, void *stream) {
-    return gemm_matmul_t_swiglu_bwd_cfg(dY, W, GATE, UP, dGATE, dUP, M, K, N, -1, stream);
+    return gemm_matmul_t_swiglu_bwd_ex(dY, W, GATE, UP, dGATE, dUP, M, K, N, nullptr, stream);
+}
+
+int64_t gemm_bwd_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int swiglu, int config) {
+    if ((op != 1 && op != 2) || M < 0 || K < 0 || N < 0 || config < -1 || config >= kNumBwdConfigs) return -1;
+    // kernel dimensions: output rows, contraction, output columns
+    const int64_t km = op == 1 ? M : K, kk = op == 1 ? N : M, kn = op == 1 ? K : N;
+    if (km == 0 || kn == 0 || kk == 0) return 0;
+    const int cfg = config >= 0 ? config
+                                : select_bwd_config(op == 1 ? kOpNT : kOpTN, km, kk, kn, op == 2 ? swiglu : 0, true);
+    return cfg < 0 ? -1 : split_workspace_bytes(kBwdConfigs[cfg], km, kn);
 }
 
 int gemm_bwd_num_configs(void) { return kNumBwdConfigs; }
 
-int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu) {
-    if (op == 1) return select_bwd_config(kOpNT, M, N, K, 0);
-    if (op == 2) return select_bwd_config(kOpTN, K, M, N, swiglu);
+int gemm_bwd_select_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, int with_workspace) {
+    if (op == 1) return select_bwd_config(kOpNT, M, N, K, 0, with_workspace != 0);
+    if (op == 2) return select_bwd_config(kOpTN, K, M, N, swiglu, with_workspace != 0);
     return -1;
 }
 
@@ -1461,8 +1509,8 @@ const char *gemm_config_name(int config) {
     return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : nullptr;
 }
 
-int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16) {
-    return select_config(M, K, N, swiglu, w_f16);
+int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16, int with_workspace) {
+    return select_config(M, K, N, swiglu, w_f16, with_workspace != 0);
 }
 
 const char *gemm_status_string(int status) {
@@ -1470,11 +1518,12 @@ const char *gemm_status_string(int status) {
         case GEMM_OK: return "ok";
         case GEMM_ERR_NULL: return "a required pointer is NULL";
         case GEMM_ERR_SHAPE: return "bad shape (negative or too large, or K or N not a multiple of 4)";
-        case GEMM_ERR_ALIGN: return "misaligned array (fp32 needs 16 bytes, binary16 W needs 8)";
+        case GEMM_ERR_ALIGN: return "misaligned array (fp32 needs 16 bytes, binary16 W 8, the workspace 256)";
         case GEMM_ERR_DTYPE: return "unknown flags or weight type";
-        case GEMM_ERR_ALIAS: return "output overlaps an input";
+        case GEMM_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
         case GEMM_ERR_CONFIG: return "tile configuration index out of range";
+        case GEMM_ERR_WORKSPACE: return "the workspace is missing or smaller than the configuration needs";
         default: return "unknown status";
     }
 }
