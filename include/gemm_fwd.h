@@ -154,6 +154,23 @@ int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const 
                        int64_t M, int64_t K, int64_t N, int w_dtype, const gemm_opts *opts, void *stream);
 
 /*
+ * For callers that cannot allocate device memory or hand in a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gemm_fwd_swiglu_ex with the library's choice and a workspace
+ * the library holds itself, a file-scope device array of 4 MiB + 64 KiB per
+ * GPU, kept until the process ends.  Same arguments, results and errors as
+ * gemm_fwd_swiglu; a shape whose split-K would need a larger workspace gives
+ * GEMM_ERR_WORKSPACE (the library's choice splits K only for outputs of at
+ * most 2^19 elements, which always fit).  Nothing is allocated or freed; the
+ * first call on a GPU also enqueues a clear of the array's counter block on
+ * `stream`.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (different streams or host threads) race: order
+ * them on one stream, or with events.
+ */
+int gemm_fwd_swiglu_noalloc(const float *GATE, const float *UP, const void *W, const float *R, float *Y,
+                            int64_t M, int64_t K, int64_t N, int w_dtype, void *stream);
+
+/*
  * Bytes of workspace a forward call needs: for `config` (>= 0), or for the
  * library's choice when a workspace is given (config = -1); 0 when that
  * configuration does not split K.  swiglu is 0/1, flags as for gemm_fwd.

@@ -22,6 +22,7 @@ _lib = None
 
 EXPORTED = (
     "gemm_fwd", "gemm_fwd_swiglu", "gemm_fwd_ex", "gemm_fwd_swiglu_ex", "gemm_fwd_workspace_bytes",
+    "gemm_fwd_swiglu_noalloc",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config", "gemm_status_string",
     "gemm_matmul_t", "gemm_matmul_at", "gemm_matmul_at_swiglu_a", "gemm_matmul_t_ex", "gemm_matmul_at_ex",
     "gemm_matmul_at_swiglu_a_ex", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
@@ -71,6 +72,8 @@ def load_library():
     lib.gemm_fwd_ex.restype = c_int
     lib.gemm_fwd_swiglu_ex.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, o, p]
     lib.gemm_fwd_swiglu_ex.restype = c_int
+    lib.gemm_fwd_swiglu_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, c_int, p]
+    lib.gemm_fwd_swiglu_noalloc.restype = c_int
     lib.gemm_fwd_workspace_bytes.argtypes = [i64, i64, i64, c_int, u32, c_int]
     lib.gemm_fwd_workspace_bytes.restype = i64
     lib.gemm_num_configs.argtypes = []

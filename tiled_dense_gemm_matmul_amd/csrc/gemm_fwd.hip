@@ -51,6 +51,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_fwd.h"
@@ -1382,6 +1383,43 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// library-held workspace of gemm_fwd_swiglu_noalloc
+// ---------------------------------------------------------------------------
+
+// For callers that cannot allocate device memory, gemm_fwd_swiglu_noalloc
+// takes its split-K workspace from this array: the counter block plus 4 MiB
+// of partial slots, enough for every split the library's choice makes
+// (outputs of at most 2^19 elements, K split in two).  Zero at load; every
+// completed call leaves its counter block zero again.  Each GPU holds its
+// own copy until the process ends.
+constexpr int64_t kScratchBytes = kCounterBytes + (4 << 20);
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+// The device address of `scratch` on the current device, fetched once per
+// device (the array's name is only a host-side stand-in in host code).  On
+// the first call on a device the counter block is also cleared, by a fill
+// kernel on the caller's stream.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void **out, hipStream_t s) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GEMM_ERR_LAUNCH;
+        hipLaunchKernelGGL(fill_k0_kernel, dim3((unsigned)ceil_div(kCounterBytes / 4, 256)), dim3(256), 0, s, nullptr,
+                           static_cast<float *>(ptr), kCounterBytes / 4);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_LAUNCH;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GEMM_OK;
+}
+
 int fwd_flags(uint32_t flags, bool &w16) {
     if (flags & ~GEMM_FLAG_W_F16) return GEMM_ERR_DTYPE;
     w16 = (flags & GEMM_FLAG_W_F16) != 0;
@@ -1423,6 +1461,18 @@ int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const 
 int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const float *R, float *Y, int64_t M,
                     int64_t K, int64_t N, int w_dtype, void *stream) {
     return gemm_fwd_swiglu_ex(GATE, UP, W, R, Y, M, K, N, w_dtype, nullptr, stream);
+}
+
+int gemm_fwd_swiglu_noalloc(const float *GATE, const float *UP, const void *W, const float *R, float *Y, int64_t M,
+                            int64_t K, int64_t N, int w_dtype, void *stream) {
+    if (w_dtype != GEMM_W_F32 && w_dtype != GEMM_W_F16) return GEMM_ERR_DTYPE;
+    const int64_t need = gemm_fwd_workspace_bytes(M, K, N, 1, w_dtype == GEMM_W_F16 ? GEMM_FLAG_W_F16 : 0u, -1);
+    if (need > kScratchBytes) return GEMM_ERR_WORKSPACE;   // (negative: a bad shape, reported by run)
+    Opts o;
+    const int st = scratch_address(&o.ws, static_cast<hipStream_t>(stream));
+    if (st != GEMM_OK) return st;
+    o.ws_bytes = kScratchBytes;
+    return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, o, stream);
 }
 
 int64_t gemm_fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int swiglu, uint32_t flags, int config) {
