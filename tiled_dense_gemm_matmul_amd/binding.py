@@ -53,15 +53,31 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+SYNC_CHECK_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmfwd_sync.so")
+_sync_lib = None
+
+
 def load_library():
     """Load libgemmfwd.so (after torch, so both share torch's HIP runtime)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
+    if _lib is None:
+        _lib = _open(_LIB_PATH)
+    return _lib
+
+
+def load_sync_check_library():
+    """The verification build (same C ABI; see the race-check tests)."""
+    global _sync_lib
+    if _sync_lib is None:
+        _sync_lib = _open(SYNC_CHECK_LIB_PATH)
+    return _sync_lib
+
+
+def _open(path):
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
-    lib = ctypes.CDLL(_LIB_PATH)
+            f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
     p, i64, u32, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int
     lib.gemm_fwd.argtypes = [p, p, p, p, i64, i64, i64, u32, p]
     lib.gemm_fwd.restype = c_int
@@ -112,7 +128,6 @@ def load_library():
     lib.act_ffn_gelu_backward.restype = c_int
     lib.act_gelu_inplace.argtypes = [p, p, i64, p]
     lib.act_gelu_inplace.restype = c_int
-    _lib = lib
     return lib
 
 

@@ -15,6 +15,7 @@ LOSS_SRC = os.path.join(PKG, "csrc", "loss.hip")
 ACT_SRC = os.path.join(PKG, "csrc", "activation.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemmfwd.so")
+SYNC_LIB = os.path.join(PKG, "libgemmfwd_sync.so")
 PROBE_SRC = os.path.join(PKG, "csrc", "mfma_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libmfmaprobe.so")
 
@@ -24,10 +25,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def _hipcc(srcs, lib: str, verbose: bool) -> str:
+def _hipcc(srcs, lib: str, verbose: bool, defines=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = lib + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *srcs, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -41,6 +42,13 @@ def build_library(verbose: bool = False) -> str:
     return _hipcc([SRC, LOSS_SRC, ACT_SRC], LIB, verbose)
 
 
+def build_sync_check_library(verbose: bool = False) -> str:
+    """The verification build of the same sources (GEMM_SYNC_CHECK: full
+    waits before every barrier, fences around the split-K exchange), which
+    the race-check tests compare bit for bit with the shipping library."""
+    return _hipcc([SRC, LOSS_SRC, ACT_SRC], SYNC_LIB, verbose, defines=("GEMM_SYNC_CHECK",))
+
+
 def build_probe(verbose: bool = False) -> str:
     """The MFMA ceiling probe used by bench.py --mfma-ceiling."""
     return _hipcc([PROBE_SRC], PROBE_LIB, verbose)
@@ -48,4 +56,5 @@ def build_probe(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_sync_check_library(verbose=True))
     print(build_probe(verbose=True))

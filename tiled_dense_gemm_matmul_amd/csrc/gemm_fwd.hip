@@ -204,6 +204,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 
+// Verification build (compiled with -DGEMM_SYNC_CHECK, a second library
+// beside the shipping one): every barrier of the GEMM kernels first waits
+// for all outstanding memory operations (s_waitcnt 0), the waits for
+// LDS-destination loads wait for every load instead of all but the later
+// stages' register loads, and the split-K exchange adds device-scope fences
+// around the arrival count.  Same arithmetic in the same order, so its
+// results must equal the shipping build's bit for bit; a difference would
+// expose a hand-counted wait or an ordering that relies on timing.
+#ifdef GEMM_SYNC_CHECK
+constexpr bool kSyncCheck = true;
+#else
+constexpr bool kSyncCheck = false;
+#endif
+
+__device__ __forceinline__ void stage_barrier() {
+    if constexpr (kSyncCheck) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
 // Out-of-range stores (offset >= resource size) are dropped by the hardware.
 __device__ __forceinline__ void store_f32x4(Rsrc r, int off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, 0);
@@ -482,7 +501,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     // Wait until at most the register loads of the last n stages are
     // outstanding, so every LDS-destination load issued before them landed.
     auto dma_wait = [&](auto n) {
-        if constexpr (DMA_A || DMA_W) wait_vmcnt<decltype(n)::value * REG_LOADS>();
+        if constexpr (DMA_A || DMA_W) wait_vmcnt<kSyncCheck ? 0u : decltype(n)::value * REG_LOADS>();
     };
 
     auto load_stage = [&](Regs &r, int k0) {
@@ -698,7 +717,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     for (int j = 0; j < PF; ++j) load_stage(r[j], kbeg + j * BK);
                     store_stage(r[0], 0);
                     dma_wait(std::integral_constant<unsigned, PF - 1>{});
-                    __syncthreads();
+                    stage_barrier();
                     int s = 0;
                     for (; s + PF <= nstages; s += PF) {
 #pragma unroll
@@ -708,7 +727,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                             store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
                             interleave_hint();
                             dma_wait(std::integral_constant<unsigned, 1>{});
-                            __syncthreads();
+                            stage_barrier();
                         }
                     }
 #pragma unroll
@@ -717,7 +736,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                             dma_stage((s + j + 1) & 1, kbeg + (s + j + 1) * BK);
                             store_stage(r[(j + 1) % PF], (s + j + 1) & 1);
                             dma_wait(std::integral_constant<unsigned, 0>{});
-                            __syncthreads();
+                            stage_barrier();
                         }
                     }
                 } else if constexpr (C::PF == 2) {
@@ -726,15 +745,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     load_stage(r1, kbeg + BK);
                     store_stage(r0, 0);
                     load_stage(r0, kbeg + 2 * BK);
-                    __syncthreads();
+                    stage_barrier();
                     for (int s = 0;; s += 2) {
                         store_stage(r1, 1);
                         load_stage(r1, kbeg + (s + 3) * BK);
-                        __syncthreads();
+                        stage_barrier();
                         if (s + 1 >= nstages) break;
                         store_stage(r0, 0);
                         load_stage(r0, kbeg + (s + 4) * BK);
-                        __syncthreads();
+                        stage_barrier();
                         if (s + 2 >= nstages) break;
                     }
                 } else {
@@ -742,27 +761,27 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     load_stage(r0, kbeg + 0);
                     store_stage(r0, 0);
                     load_stage(r0, kbeg + BK);
-                    __syncthreads();
+                    stage_barrier();
                     for (int s = 0;; ++s) {
                         store_stage(r0, (s + 1) & 1);
                         load_stage(r0, kbeg + (s + 2) * BK);
-                        __syncthreads();
+                        stage_barrier();
                         if (s + 1 >= nstages) break;
                     }
                 }
             }
-            __syncthreads();  // the epilogue's barrier
+            stage_barrier();  // the epilogue's barrier
             if constexpr (KS > 1) {
-                __syncthreads();  // partials stored
-                __syncthreads();  // arrival counted
+                stage_barrier();  // partials stored
+                stage_barrier();  // arrival counted
             }
             return;
         }
         if (nstages > 0) {
-            __syncthreads();
+            stage_barrier();
             for (int s = 0;; ++s) {
                 compute_stage(s & 1);
-                __syncthreads();
+                stage_barrier();
                 if (s + 1 >= nstages) break;
             }
         }
@@ -772,33 +791,33 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             load_stage(r0, kbeg + 0);
             load_stage(r1, kbeg + BK);
             store_stage(r0, 0);
-            __syncthreads();
+            stage_barrier();
             for (int s = 0;; s += 2) {
                 load_stage(r0, kbeg + (s + 2) * BK);
                 compute_stage(0);
                 store_stage(r1, 1);
-                __syncthreads();
+                stage_barrier();
                 if (s + 1 >= nstages) break;
                 load_stage(r1, kbeg + (s + 3) * BK);
                 compute_stage(1);
                 store_stage(r0, 0);
-                __syncthreads();
+                stage_barrier();
                 if (s + 2 >= nstages) break;
             }
         } else {
             Regs r0;
             load_stage(r0, kbeg + 0);
             store_stage(r0, 0);
-            __syncthreads();
+            stage_barrier();
             for (int s = 0;; ++s) {
                 load_stage(r0, kbeg + (s + 1) * BK);
                 compute_stage(s & 1);
                 if (s + 1 >= nstages) break;
                 store_stage(r0, (s + 1) & 1);
-                __syncthreads();
+                stage_barrier();
             }
             // the last stage was read without a closing barrier
-            __syncthreads();
+            stage_barrier();
         }
     }
 
@@ -819,7 +838,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 for (int r = 0; r < 4; ++r)
                     Ct[(wm * WTM + i * 16 + q4 * 4 + r) * CSTR + wn * WTN + j * 16 + r16] = acc[i][j][r];
     }
-    __syncthreads();
+    stage_barrier();
 
     const size_t tile_off = (size_t)m0 * N + n0;
     // The last step of the epilogue for four consecutive outputs at byte
@@ -872,12 +891,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         // whole L2 of the XCD instead.)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if constexpr (kSyncCheck) __threadfence();
+        stage_barrier();
         if (tid == 0)
             sk_last = __hip_atomic_fetch_add(p.cnt + tile_id, 1u, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(KS - 1);
-        __syncthreads();
+        stage_barrier();
         if (!sk_last || !computes) return;
+        if constexpr (kSyncCheck) __threadfence();
         if (tid == 0)
             __hip_atomic_store(p.cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int ybytes = rows_valid * N * 4;
@@ -1035,6 +1056,8 @@ constexpr int64_t kSplitMaxElems = (int64_t)1 << 19;
 // call), then KS partial slots of M x N floats.
 constexpr int64_t kCounterBytes = 64 << 10;
 constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+// Size of the library-held workspace of gemm_fwd_swiglu_noalloc (below).
+constexpr int64_t kScratchBytes = kCounterBytes + (4 << 20);
 
 // Bytes a split-K configuration needs for an M x N output; zero for a
 // configuration without split-K, -1 for one with more output tiles than the
@@ -1196,7 +1219,12 @@ struct Opts {
     void *ws = nullptr;
     int64_t ws_bytes = 0;
     void *start = nullptr, *stop = nullptr;
+    // the workspace is the library-held array (gemm_fwd_swiglu_noalloc),
+    // resolved only once the arguments have passed validation
+    bool library_scratch = false;
 };
+
+int scratch_address(void **out, hipStream_t s);
 
 int read_opts(const gemm_opts *o, int num_configs, Opts &out) {
     if (o == nullptr) return GEMM_OK;
@@ -1276,7 +1304,13 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
 
     Params p;
     int cfg = -1;
-    const int st = resolve(kConfigs, o, M, N,
+    Opts oo = o;
+    if (o.library_scratch) {
+        const int sa = scratch_address(&oo.ws, s);
+        if (sa != GEMM_OK) return sa;
+        oo.ws_bytes = kScratchBytes;
+    }
+    const int st = resolve(kConfigs, oo, M, N,
                            [&](bool split) { return select_config(M, K, N, swiglu, w16, split); }, p, cfg);
     if (st != GEMM_OK) return st;
     const ConfigEntry &e = kConfigs[cfg];
@@ -1393,7 +1427,6 @@ int run_bwd(int op, bool swiglu, const float *A, const float *U, const float *B,
 // (outputs of at most 2^19 elements, K split in two).  Zero at load; every
 // completed call leaves its counter block zero again.  Each GPU holds its
 // own copy until the process ends.
-constexpr int64_t kScratchBytes = kCounterBytes + (4 << 20);
 static __device__ __align__(256) float scratch[kScratchBytes / 4];
 
 // The device address of `scratch` on the current device, fetched once per
@@ -1469,9 +1502,7 @@ int gemm_fwd_swiglu_noalloc(const float *GATE, const float *UP, const void *W, c
     const int64_t need = gemm_fwd_workspace_bytes(M, K, N, 1, w_dtype == GEMM_W_F16 ? GEMM_FLAG_W_F16 : 0u, -1);
     if (need > kScratchBytes) return GEMM_ERR_WORKSPACE;   // (negative: a bad shape, reported by run)
     Opts o;
-    const int st = scratch_address(&o.ws, static_cast<hipStream_t>(stream));
-    if (st != GEMM_OK) return st;
-    o.ws_bytes = kScratchBytes;
+    o.library_scratch = true;
     return run(true, GATE, UP, W, w_dtype == GEMM_W_F16, R, Y, M, K, N, o, stream);
 }
 
