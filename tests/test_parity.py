@@ -3,9 +3,10 @@ element, in the launch configuration the library selects (the one bench.py
 times).  Tolerances: |y - y_ref| <= 2e-5 * sum_k|a_ik||w_kj| + 1e-6 for fp32
 weights and 1e-3 * sum_k|a_ik||w_kj| + 1e-5 for binary16 weights.
 
-The two largest cases (M = 8192 / 8191) are checked element-wise on a sample
-of rows that includes the whole last (partial) tile, and in every row and
-column through the exact row/column sums of the product."""
+The two largest cases (M = 8192 / 8191) are checked element-wise on every
+row too, in blocks of rows against the threaded oracle, and in addition
+through the exact row/column sums of the product; Y sits in a buffer whose
+tail must stay untouched."""
 import numpy as np
 import pytest
 
@@ -55,11 +56,15 @@ def cfg5():
     return inputs.cfg5()
 
 
-def _sample_rows(M, seed, count=96):
-    rng = np.random.default_rng(seed)
-    tail_start = (M - 1) // 64 * 64 - 64        # the last two 64-row tiles, whole
-    rows = np.concatenate([rng.choice(tail_start, size=count, replace=False), np.arange(tail_start, M)])
-    return np.unique(rows)
+def _check_every_row(c, y, label, block=1024):
+    """Element-wise parity of every row of y, block by block of rows."""
+    M = y.shape[0]
+    worst, fails = 0.0, 0
+    for r0 in range(0, M, block):
+        rows = np.arange(r0, min(M, r0 + block), dtype=np.int64)
+        res = check(c, y[rows], rows=rows, label=f"{label} rows {r0}..{rows[-1]}")
+        worst, fails = max(worst, res["max_ratio"]), fails + res["fails"]
+    say(f"  {label}: every row, max err/tol {worst:.4g}, fails {fails}")
 
 
 def _guarded_run(case, M, N):
@@ -81,8 +86,7 @@ def test_cfg5a_swiglu_down_w16(cfg5, M):
          "W": cfg5["W_down"], "R": np.ascontiguousarray(cfg5["R"][:M])}
     say(f"cfg5a matmul_residual_swiglu_a_w16 {M}x3072x768 seed 4")
     y = _host(_guarded_run(c, M, 768))
-    rows = _sample_rows(M, 50 + M)
-    check(c, y[rows], rows=rows, label=f"cfg5a M={M} sampled rows")
+    _check_every_row(c, y, f"cfg5a M={M}")
     check_sums(c, y, label=f"cfg5a M={M}")
 
 
@@ -91,6 +95,5 @@ def test_cfg5b_lm_head_w16(cfg5, M):
     c = {"X": np.ascontiguousarray(cfg5["X"][:M]), "W": cfg5["W_lm"]}
     say(f"cfg5b matmul_w16 lm_head {M}x768x50304 seed 4")
     y = _host(_guarded_run(c, M, 50304))
-    rows = _sample_rows(M, 70 + M, count=32)
-    check(c, y[rows], rows=rows, label=f"cfg5b M={M} sampled rows")
+    _check_every_row(c, y, f"cfg5b M={M}")
     check_sums(c, y, label=f"cfg5b M={M}")
