@@ -988,6 +988,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp4_pf2_dAW"),
     make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
     make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
@@ -1092,11 +1093,15 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // than 128 x 192 on the shapes measured.  And 64 x 64 tiles
 // rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
 // and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
+// The smallest forward grids stage 128-deep slices of K two at a time: at
+// 512 x 768 x 768, one 32 x 48 tile per CU, 7.9 against 9.4 us with 64-deep
+// slices three at a time (8.2 against 9.8 with R), timed between the other
+// products of the seq-512 layer.
 // Long K on a small grid splits K over two workgroups when the caller
 // provides a workspace (`split`); the forward SwiGLU product then stages
 // 128-deep slices of K (512 x 3072 x 768: 26.5 against 26.9 us with 64).
 // `forward` false: the rule as the backward products measured it, without
-// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep split.
+// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep slices.
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward = true) {
     (void)w16;
     static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
@@ -1106,6 +1111,7 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     static const int mid = config_index("64x64x64_w2x2_sp4_dAW");
     static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il_dA");
     static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
+    static const int small128 = config_index("32x48x128_k4_sp4_pf2_dAW");
     static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
     static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
     static const int deep_split128 = config_index("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
@@ -1113,7 +1119,7 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
     // a name missing from the table is a build error in spirit: report it
     // as an unavailable configuration rather than run another one
     static const bool complete = big >= 0 && swiglu_wide >= 0 && wide >= 0 && tall >= 0 && mid >= 0 &&
-                                 narrow >= 0 && small >= 0 && deep >= 0 && deep_split >= 0 &&
+                                 narrow >= 0 && small >= 0 && small128 >= 0 && deep >= 0 && deep_split >= 0 &&
                                  deep_split128 >= 0 && tiny >= 0;
     if (!complete) return -1;
     const int64_t cus = 256;
@@ -1135,7 +1141,7 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
             return forward && swiglu ? deep_split128 : deep_split;
         return deep;
     }
-    return small;
+    return forward ? small128 : small;
 }
 
 // Tile choice for the backward products, by their kernel dimensions (output
