@@ -17,7 +17,12 @@ divided by the wall time per step.  The roofline object describes the
 dominant kernel (lm_head) against the fp32 matrix-core peak of MI355X, with
 its average duration taken from HIP events that the launch itself records at
 the kernel's start and end (gemm_opts.start_event / stop_event of the _ex
-entry points) for each of its launches in the timed region.  Every product
+entry points) for each of its launches in the timed region.  The events are
+the library's timing events (gemm_timing_event_create): a default HIP timing
+event writes back and invalidates the caches at system scope when it is
+recorded, which lengthens the timed kernel by about 2 us and delays the next
+launch by about 5 us per step; these record the same start and end times
+without it.  Every product
 goes through the _ex entry points with a workspace sized by
 gemm_fwd_workspace_bytes (only the SwiGLU down-projection splits K and uses
 it), allocated before the timed region.  The per-kernel breakdown comes from a separate pass after the
@@ -29,9 +34,10 @@ products (repeated for at least --cpu-seconds), on this host's cores.
 HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
 this script (FETCH_SIZE, then WRITE_SIZE) and two of its --copy-calibration
 mode (a plain device copy of a known size), turned into bytes per launch by
---traffic-from and kept in profiles/lm_head_traffic.json together with the
-hash of the kernel source they were taken on; the bench line reports them only
-while that hash still matches.
+--traffic-from (for every kernel of the step) and kept in
+profiles/lm_head_traffic.json together with the hash of the kernel source
+they were taken on; the bench line reports them only while that hash still
+matches.
 """
 from __future__ import annotations
 
@@ -50,7 +56,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3   # 256 CU x 256 flop/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "TFLOP/s of fused forward GEMMs (seq 512, d768/3072/16384); % FP32 MFMA peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_dense_gemm_matmul_amd", "csrc", "gemm_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "lm_head_traffic.json")
 
 
 def parse():
@@ -86,17 +93,23 @@ def parse():
                     help="instead of the step: time each product at the per-GPU shape of its natural sharding "
                          "over 2, 4 and 8 GPUs (lm_head and gate/up by columns, the SwiGLU down-projection by "
                          "its contraction), one GPU standing in for one shard")
+    ap.add_argument("--counter-workloads", action="store_true",
+                    help="instead of the step: launch cfg1 and the 16 x 512-token products (M = 8192 and 8191) "
+                         "in turn a few times, for rocprofv3 counter runs")
     ap.add_argument("--counters-from", metavar="DIR",
-                    help="turn the rocprofv3 counter runs under DIR (p1/, p2/) into "
-                         + os.path.relpath(os.path.join(ROOT, "profiles", "seq512_counters.md"), ROOT) + " and exit")
+                    help="turn the rocprofv3 counter runs under DIR (step/p1, step/p2, workloads/p1, workloads/p2) "
+                         "into the counter summaries under profiles/ and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
-                    help="turn the rocprofv3 counter runs under DIR (fetch/, write/, copy_fetch/, copy_write/) "
-                         "into " + os.path.relpath(TRAFFIC_FILE, ROOT) + " and exit")
+                    help="with or without --counters-from: turn the FETCH_SIZE / WRITE_SIZE runs under DIR "
+                         "(step/fetch, step/write, workloads/..., copy_fetch, copy_write) into the traffic "
+                         "summaries under profiles/ and " + os.path.relpath(TRAFFIC_FILE, ROOT) + ", and exit")
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="turn a rocprofv3 --kernel-trace run of the step (DIR/trace) and the bench line it "
+                         "printed (DIR/bench.log) into profiles/seq512_step_kernel_trace.md and exit")
     return ap.parse_args()
 
 
 COPY_BYTES = 256 << 20
-STEP_KERNELS = 5          # launches per step, lm_head last
 
 
 def copy_calibration():
@@ -108,16 +121,6 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(f"copied {COPY_BYTES} bytes 5 times", flush=True)
-
-
-def _counter_rows(run_dir):
-    import csv
-    import glob
-    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {run_dir}")
-    with open(files[0]) as f:
-        return list(csv.DictReader(f))
 
 
 BACKWARD = [
@@ -418,35 +421,152 @@ COUNTER_PASSES = {
 }
 STEP_LABELS = ["qkvo_residual", "qkvo", "ffn_down", "ffn_gate_up", "lm_head"]   # launch order in a step
 
+# The kernels of each counter set in launch order: label, M, K, N, SwiGLU,
+# f16 W, residual.  "step" is the seq-512 step (bench.py --steps 5 --warmup 2
+# --prewarm-s 0 --no-cpu); "workloads" the other workload configurations
+# (bench.py --counter-workloads), launched WORKLOAD_REPS times in turn.
+COUNTER_SETS = {
+    "step": {
+        "title": "the seq-512 forward step (bench.py)",
+        "cmd": "python3 $R/bench.py --steps 5 --warmup 2 --prewarm-s 0 --no-cpu",
+        "kernels": [("qkvo_residual", 512, 768, 768, False, False, True),
+                    ("qkvo", 512, 768, 768, False, False, False),
+                    ("ffn_down", 512, 3072, 768, True, False, True),
+                    ("ffn_gate_up", 512, 768, 3072, False, True, False),
+                    ("lm_head", 512, 768, 16384, False, True, False)],
+        "counters_md": "seq512_counters.md", "traffic_md": "seq512_traffic.md",
+    },
+    "workloads": {
+        "title": "the 128-token and 16 x 512-token workloads (bench.py --counter-workloads)",
+        "cmd": "python3 $R/bench.py --counter-workloads",
+        "kernels": [("cfg1 matmul", 128, 768, 768, False, False, False),
+                    ("cfg5a SwiGLU+R, M=8192", 8192, 3072, 768, True, True, True),
+                    ("cfg5a SwiGLU+R, M=8191", 8191, 3072, 768, True, True, True),
+                    ("cfg5b lm_head, M=8192", 8192, 768, 50304, False, True, False),
+                    ("cfg5b lm_head, M=8191", 8191, 768, 50304, False, True, False)],
+        "counters_md": "workload_counters.md", "traffic_md": "workload_traffic.md",
+    },
+}
+WORKLOADS = [
+    # the "workloads" counter set: generator, variant keys, M rows used
+    ("cfg1", ("X", "W", None), None),
+    ("cfg5", ("G", "U", "W_down", "R"), None),
+    ("cfg5", ("G", "U", "W_down", "R"), 8191),
+    ("cfg5", ("X", "W_lm", None), None),
+    ("cfg5", ("X", "W_lm", None), 8191),
+]
+WORKLOAD_REPS = 3
 
-def counters_from(base):
-    """Per-kernel hardware counters of the step (two rocprofv3 --pmc runs of
-    this script) as a markdown table in profiles/seq512_counters.md."""
+
+def alg_bytes(M, K, N, swiglu, w16, resid):
+    """Algorithmic HBM bytes of one launch: A (G and U with SwiGLU) and W
+    read once, R read once, Y written once."""
+    return M * K * (8 if swiglu else 4) + K * N * (2 if w16 else 4) + M * N * 4 * (2 if resid else 1)
+
+
+def counter_workloads():
+    """The "workloads" counter set: each configuration in the library's
+    choice (with its workspace), all launched in turn WORKLOAD_REPS times."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding, inputs
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    gens, launches = {}, []
+    for (gen, keys, rows), spec in zip(WORKLOADS, COUNTER_SETS["workloads"]["kernels"]):
+        if gen not in gens:
+            gens[gen] = getattr(inputs, gen)()
+        c = gens[gen]
+
+        def d(key, r=None):
+            a = c[key]
+            return torch.from_numpy(np.ascontiguousarray(a if r is None else a[:r])).to(dev)
+        swiglu = len(keys) == 4
+        if swiglu:
+            ts = [d(keys[0], rows), d(keys[1], rows)]
+            W, rkey = d(keys[2]), keys[3]
+        else:
+            ts = [d(keys[0], rows)]
+            W, rkey = d(keys[1]), keys[2]
+        R = d(rkey, rows) if rkey else None
+        M, K = ts[0].shape
+        N = W.shape[1]
+        w16 = W.dtype == torch.float16
+        assert (M, K, N, swiglu, w16, R is not None) == spec[1:], (spec, M, K, N)
+        Y = torch.empty((M, N), device=dev)
+        wsb = lib.gemm_fwd_workspace_bytes(M, K, N, int(swiglu), int(w16), -1)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+        o = binding.opts(-1, ws.data_ptr() if wsb else None, wsb)
+        if swiglu:
+            a = (ts[0].data_ptr(), ts[1].data_ptr(), W.data_ptr(), R.data_ptr(), Y.data_ptr(), M, K, N, int(w16))
+            launches.append((spec[0], lib.gemm_fwd_swiglu_ex, a, o, (ts, W, R, Y, ws)))
+        else:
+            a = (ts[0].data_ptr(), W.data_ptr(), None if R is None else R.data_ptr(), Y.data_ptr(), M, K, N,
+                 binding.GEMM_FLAG_W_F16 if w16 else 0)
+            launches.append((spec[0], lib.gemm_fwd_ex, a, o, (ts, W, R, Y, ws)))
+    torch.cuda.synchronize()
+    for rep in range(WORKLOAD_REPS):
+        for label, fn, a, o, _ in launches:
+            st = fn(*a, o, sp)
+            if st != 0:
+                raise RuntimeError(f"{label}: {binding.status_string(st)}")
+        torch.cuda.synchronize()
+        print(f"counter workloads: round {rep + 1} of {WORKLOAD_REPS} done", flush=True)
+
+
+def _gemm_rows(run_dir, what="counter_collection"):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", f"*{what}.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no {what}.csv under {run_dir}")
+    with open(files[0]) as f:
+        return [r for r in csv.DictReader(f) if "gemm_fwd_kernel" in r["Kernel_Name"]]
+
+
+def _by_kernel(rows, labels):
+    """Counter rows grouped by the kernel of the set that each dispatch is
+    (dispatch order modulo the set's launches)."""
+    import collections
+    order = {d: i for i, d in enumerate(sorted({int(r["Dispatch_Id"]) for r in rows}))}
+    if len(order) % len(labels):
+        raise SystemExit(f"{len(order)} GEMM dispatches is not a whole number of rounds of {len(labels)}")
+    out = collections.defaultdict(list)
+    for r in rows:
+        out[labels[order[int(r["Dispatch_Id"])] % len(labels)]].append(r)
+    return out
+
+
+def counters_table(base, set_name):
+    """Per-kernel hardware counters of a counter set from its two
+    rocprofv3 --pmc runs (base/<set>/p1, p2), as markdown."""
     import collections
     import statistics
+    cs = COUNTER_SETS[set_name]
+    labels = [k[0] for k in cs["kernels"]]
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     durs = collections.defaultdict(list)
+    clocks = collections.defaultdict(list)
     for run in COUNTER_PASSES:
-        rows = [r for r in _counter_rows(os.path.join(base, run)) if "gemm_fwd_kernel" in r["Kernel_Name"]]
-        order = {d: i for i, d in enumerate(sorted({int(r["Dispatch_Id"]) for r in rows}))}
-        for r in rows:
-            k = STEP_LABELS[order[int(r["Dispatch_Id"])] % STEP_KERNELS]
-            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
-            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
-                durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
-    shapes = {name: shape_of(case) for name, case in workload()}
+        for k, rows in _by_kernel(_gemm_rows(os.path.join(base, set_name, run)), labels).items():
+            for r in rows:
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                    durs[k].append(dur)
+                    clocks[k].append(float(r["Counter_Value"]) / 8 / dur)
     simds = 1024
-    lm_clock = statistics.mean(vals["lm_head"]["GRBM_GUI_ACTIVE"]) / 8 / statistics.median(durs["lm_head"])
     lines = [
-        "# Hardware counters of the seq-512 forward step (bench.py)",
+        f"# Hardware counters of {cs['title']}",
         "",
         "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host and $OUT an output "
         "directory), one counter set per run:",
         "",
     ]
     for run, ctrs in COUNTER_PASSES.items():
-        lines.append(f"    rocprofv3 --pmc {ctrs} -f csv -d $OUT/counters/{run} -o pmc -- "
-                     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu")
+        lines.append(f"    timeout -s KILL 120 rocprofv3 --pmc {ctrs} -f csv -d $OUT/counters/{set_name}/{run} -o pmc -- "
+                     f"{cs['cmd']}")
     lines += [
         "    python3 bench.py --counters-from $OUT/counters      # writes this file",
         "",
@@ -454,73 +574,203 @@ def counters_from(base):
         "slows the kernels (the `µs under counters` column), so the busy fractions are lower than in an",
         "unprofiled run; the instruction counts are exact.",
         "",
-        "- MFMA count / ideal = SQ_INSTS_MFMA / (2MNK / 2048), the flops of one v_mfma_f32_16x16x4_f32.",
+        "- MFMA count / ideal = SQ_INSTS_MFMA / (2MNK / 2048), the flops of one v_mfma_f32_16x16x4_f32",
+        "  (partial tiles are padded to whole 16 x 16 blocks, so a ragged M or N counts above 1).",
         "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (32 per MFMA, summed over SIMDs) / (1024 SIMDs x 2400 MHz x duration).",
-        "  The lm_head runs long enough for GRBM_GUI_ACTIVE / 8 XCDs / duration to give the clock: "
-        + f"{lm_clock:.0f} MHz.",
+        "- clock = GRBM_GUI_ACTIVE / 8 XCDs / duration: the engine clock, shown for kernels of 50 us and more",
+        "  (the counter also runs outside a short kernel's own start and end).",
         "- other VALU per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (the VALU count includes the MFMAs);",
         "  co-issue = SQ_VALU_MFMA_COEXEC_CYCLES, cycles in which a VALU instruction issued while the MFMA unit was busy.",
         "- LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).",
         "",
-        "| kernel | M×K×N | launches | µs under counters | MFMA count / ideal | MFMA busy | "
+        "| kernel | M×K×N | launches | µs under counters | clock MHz | MFMA count / ideal | MFMA busy | "
         "other VALU per MFMA | co-issue cycles | LDS instr per MFMA | LDS conflict | L2 hit |",
-        "|---|---|---|---|---|---|---|---|---|---|---|",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
-    for k in STEP_LABELS:
+    for (k, M, K, N, *_rest) in cs["kernels"]:
         v = {c: statistics.mean(x) for c, x in vals[k].items()}
         d = statistics.median(durs[k])
-        M, K, N = shapes[k]
         ideal = 2 * M * K * N / 2048
         lines.append(
             f"| {k} | {M}×{K}×{N} | {len(vals[k]['SQ_INSTS_MFMA'])} | {d:.1f} | "
+            f"{f'{statistics.median(clocks[k]):.0f}' if d >= 50 else '—'} | "
             f"{v['SQ_INSTS_MFMA'] / ideal:.3f} | {100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * 2400 * d):.1f}% | "
             f"{(v['SQ_INSTS_VALU'] - v['SQ_INSTS_MFMA']) / v['SQ_INSTS_MFMA']:.2f} | "
             f"{v['SQ_VALU_MFMA_COEXEC_CYCLES']:.0f} | "
             f"{v['SQ_INSTS_LDS'] / v['SQ_INSTS_MFMA']:.3f} | "
             f"{100 * v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.1f}% | "
             f"{100 * v['TCC_HIT_sum'] / (v['TCC_HIT_sum'] + v['TCC_MISS_sum']):.1f}% |")
-    out = os.path.join(ROOT, "profiles", "seq512_counters.md")
-    with open(out, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    return lines
 
 
-def traffic_from(base):
-    """HBM bytes per lm_head launch from FETCH_SIZE / WRITE_SIZE runs, each
-    scaled by what the same counter reads for a copy of COPY_BYTES."""
-    import numpy as np
+def traffic_table(base, set_name):
+    """HBM bytes per launch of each kernel of a counter set from its
+    FETCH_SIZE and WRITE_SIZE runs (base/<set>/fetch, write), each scaled by
+    what the same counter reads for a plain copy of COPY_BYTES (base/copy_fetch,
+    copy_write), as markdown plus a dict per kernel."""
+    import statistics
+    cs = COUNTER_SETS[set_name]
+    labels = [k[0] for k in cs["kernels"]]
 
     def copy_kib(run):
-        vals = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(base, run))
-                if "copy" in r["Kernel_Name"].lower()]
-        return float(np.median(vals))
-
-    def lm_head_kib(run):
-        rows = [r for r in _counter_rows(os.path.join(base, run)) if "gemm_fwd_kernel" in r["Kernel_Name"]]
-        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        vals = [float(r["Counter_Value"]) for i, r in enumerate(rows) if i % STEP_KERNELS == STEP_KERNELS - 1]
-        return float(np.mean(vals)), len(vals)
+        import csv
+        import glob
+        f = glob.glob(os.path.join(base, run, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(base, run)}")
+        with open(f[0]) as fh:
+            vals = [float(r["Counter_Value"]) for r in csv.DictReader(fh) if "copy" in r["Kernel_Name"].lower()]
+        return statistics.median(vals)
 
     f_scale = COPY_BYTES / (copy_kib("copy_fetch") * 1024)
     w_scale = COPY_BYTES / (copy_kib("copy_write") * 1024)
-    fetch_kib, n_f = lm_head_kib("fetch")
-    write_kib, n_w = lm_head_kib("write")
-    fetch = fetch_kib * 1024 * f_scale
-    write = write_kib * 1024 * w_scale
-    out = {
-        "kernel_sha256_16": kernel_hash(),
-        "kernel": "lm_head (matmul_w16 512x768x16384)",
-        "bytes_per_launch": round(fetch + write),
-        "fetch_bytes": round(fetch), "write_bytes": round(write),
-        "fetch_size_kib_raw": round(fetch_kib, 1), "write_size_kib_raw": round(write_kib, 1),
-        "copy_scale": {"FETCH_SIZE": round(f_scale, 4), "WRITE_SIZE": round(w_scale, 4)},
-        "algorithmic_bytes": 512 * 768 * 4 + 768 * 16384 * 2 + 512 * 16384 * 4,
-        "dispatches": {"fetch": n_f, "write": n_w},
-    }
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    print(json.dumps(out))
+    fetch = {k: [float(r["Counter_Value"]) for r in rows]
+             for k, rows in _by_kernel(_gemm_rows(os.path.join(base, set_name, "fetch")), labels).items()}
+    write = {k: [float(r["Counter_Value"]) for r in rows]
+             for k, rows in _by_kernel(_gemm_rows(os.path.join(base, set_name, "write")), labels).items()}
+    lines = [
+        f"# HBM traffic of {cs['title']}",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host and $OUT an output "
+        "directory), one counter per run:",
+        "",
+        f"    timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/traffic/{set_name}/fetch -o pmc -- {cs['cmd']}",
+        f"    timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/traffic/{set_name}/write -o pmc -- {cs['cmd']}",
+        "    timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/traffic/copy_fetch -o pmc -- "
+        "python3 $R/bench.py --copy-calibration",
+        "    timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/traffic/copy_write -o pmc -- "
+        "python3 $R/bench.py --copy-calibration",
+        "    python3 bench.py --counters-from $OUT/counters --traffic-from $OUT/traffic      # writes this file",
+        "",
+        f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE = {copy_kib('copy_fetch') / 1024:.0f} MiB "
+        f"and WRITE_SIZE = {copy_kib('copy_write') / 1024:.0f} MiB per dispatch, so FETCH_SIZE is scaled by "
+        f"{f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.  Averages over every launch of each kernel; "
+        f"kernel source hash at measurement: {kernel_hash()}.",
+        "",
+        "Algorithmic bytes: A (G and U with SwiGLU) and W read once, R read once, Y written once.",
+        "",
+        "FETCH_SIZE and WRITE_SIZE count what the L2 caches read from and write to the memory side of the chip:",
+        "each XCD's L2 fetches its own copy of whatever its tiles read, and reads that the 256 MB Infinity Cache",
+        "serves count as well, so the fetched bytes are an upper bound of the HBM reads.",
+        "",
+        "| kernel | M×K×N | launches | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | fetched bytes | written bytes | "
+        "algorithmic reads | algorithmic writes | fetched / alg. reads | written / alg. writes |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    per = {}
+    for (k, M, K, N, swiglu, w16, resid) in cs["kernels"]:
+        fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
+        fb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
+        ar = alg_bytes(M, K, N, swiglu, w16, resid) - M * N * 4
+        aw = M * N * 4
+        per[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "fetch_size_kib_raw": round(fk, 1),
+                  "write_size_kib_raw": round(wk, 1), "algorithmic_bytes": ar + aw,
+                  "dispatches": {"fetch": len(fetch[k]), "write": len(write[k])},
+                  "copy_scale": {"FETCH_SIZE": round(f_scale, 4), "WRITE_SIZE": round(w_scale, 4)}}
+        lines.append(f"| {k} | {M}×{K}×{N} | {len(fetch[k])} | {fk:.1f} | {wk:.1f} | {fb:,.0f} | {wb:,.0f} | "
+                     f"{ar:,} | {aw:,} | {fb / ar:.2f} | {wb / aw:.2f} |")
+    return lines, per
+
+
+def counters_from(counters_base, traffic_base=None, out_dir=PROFILES):
+    """Write the counter (and, with traffic_base, the HBM traffic) summaries
+    of every counter set found under the run directories into out_dir, and
+    the lm_head's bytes per launch into the traffic file bench.py reads
+    (lm_head_traffic.json there)."""
+    for set_name, cs in COUNTER_SETS.items():
+        if counters_base and os.path.isdir(os.path.join(counters_base, set_name)):
+            lines = counters_table(counters_base, set_name)
+            with open(os.path.join(out_dir, cs["counters_md"]), "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print("\n".join(lines))
+        if traffic_base and os.path.isdir(os.path.join(traffic_base, set_name)):
+            lines, per = traffic_table(traffic_base, set_name)
+            with open(os.path.join(out_dir, cs["traffic_md"]), "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print("\n".join(lines))
+            if set_name == "step":
+                lm = per["lm_head"]
+                out = {"kernel_sha256_16": kernel_hash(), "kernel": "lm_head (matmul_w16 512x768x16384)",
+                       "bytes_per_launch": lm["fetch_bytes"] + lm["write_bytes"], **lm}
+                with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+                    json.dump(out, f, indent=1)
+                    f.write("\n")
+
+
+def trace_from(base, out_dir=PROFILES):
+    """profiles/seq512_step_kernel_trace.md from a rocprofv3 --kernel-trace
+    --stats run of the step (base/trace) and the bench line that run printed
+    (base/bench.log): every launch of each step kernel, and the launches of
+    the timed region alone against the HIP-event figure the bench line
+    reports for them."""
+    import statistics
+    with open(os.path.join(base, "bench.log")) as f:
+        line = json.loads([l for l in f if l.startswith("{")][-1])
+    rows = _gemm_rows(os.path.join(base, "trace"), "kernel_trace")
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    n = len(STEP_LABELS)
+    steps, warm, pre = line["steps"], line["warmup"], line["prewarm_steps"]
+    nb = min(steps, 50)
+    if len(rows) != n * (pre + warm + steps + nb):
+        raise SystemExit(f"{len(rows)} GEMM dispatches, expected {n} x ({pre} + {warm} + {steps} + {nb})")
+    t0, t1 = n * (pre + warm), n * (pre + warm + steps)
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in rows]
+
+    def pick(i, lo, hi):
+        return [dur[j] for j in range(lo, hi) if j % n == i]
+
+    flops = {k: 2 * M * K * N for (k, M, K, N, *_r) in COUNTER_SETS["step"]["kernels"]}
+    cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/profiles/trace -o bench -- "
+           f"python3 $R/bench.py --steps {steps} --warmup {warm} --no-cpu")
+    lines = [
+        "# Kernel trace of the seq-512 forward step (bench.py)",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host):",
+        "",
+        "    python3 $R/bench.py > $R/gpurun_out/profiles/bench_plain.log      # unprofiled, for comparison",
+        f"    {cmd} > $R/gpurun_out/profiles/bench.log",
+        "    python3 bench.py --trace-from gpurun_out/profiles      # writes this file",
+        "",
+        f"Kernel source hash {kernel_hash()}.  The run made {pre} time-based pre-warm steps, {warm} counted warm-up "
+        f"steps, the {steps} timed steps and a pass of {nb} steps with events on every launch: "
+        f"{len(rows)} GEMM launches in all.",
+        "",
+        "| kernel | timed-region launches | rocprof avg µs | min | max | % of 157.3 at avg | all launches | "
+        f"rocprof avg µs (all) | event pass: rocprof avg µs | event pass: bench.py event avg µs |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for i, k in enumerate(STEP_LABELS):
+        t = pick(i, t0, t1)
+        a = pick(i, 0, len(rows))
+        e = pick(i, t1, len(rows))
+        avg = statistics.mean(t)
+        lines.append(f"| {k} | {len(t)} | {avg:.2f} | {min(t):.2f} | {max(t):.2f} | "
+                     f"{100 * flops[k] / avg / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1f} | {len(a)} | {statistics.mean(a):.2f} | "
+                     f"{statistics.mean(e):.2f} | {line['kernels'][k]['avg_us']:.2f} |")
+    lm = pick(STEP_LABELS.index("lm_head"), t0, t1)
+    lines += [
+        "",
+        f"Same run, bench.py line: {line['ms_per_step'] * 1e3:.1f} us per step, {line['value']} TFLOP/s; its roofline "
+        f"kernel lm_head averaged {line['roofline']['avg_us']} us by HIP events over the {steps} timed-region launches, "
+        f"against {statistics.mean(lm):.2f} us by the trace over the same launches.  Under the profiler the events "
+        "read a few microseconds long and the step runs slower.",
+    ]
+    plain = os.path.join(base, "bench_plain.log")
+    if os.path.exists(plain):
+        with open(plain) as f:
+            pl = json.loads([l for l in f if l.startswith("{")][-1])
+        lines += [
+            "",
+            f"The unprofiled run of the same command in the same session (bench_plain.log): "
+            f"{pl['ms_per_step'] * 1e3:.1f} us per step, {pl['value']} TFLOP/s; lm_head averaged "
+            f"{pl['roofline']['avg_us']} us by HIP events over its {pl['roofline']['launches']} timed-region launches "
+            f"({100 * (pl['roofline']['avg_us'] / statistics.mean(lm) - 1):+.1f}% against the trace above), "
+            f"{pl['roofline']['frac'] * 100:.1f}% of {PEAK_FP32_MFMA_TFLOPS} TFLOP/s.",
+        ]
+    out = os.path.join(out_dir, "seq512_step_kernel_trace.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def kernel_hash():
@@ -681,17 +931,13 @@ def time_configs():
         def sample(n, flush_between):
             """n launches queued back to back (a flush kernel between them
             when cold), each timed by its own event pair; read at the end."""
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            for a, b in evs:
-                a.record(st)
-                b.record(st)
-            torch.cuda.synchronize()
+            evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
             for a, b in evs:
                 if flush_between:
                     flush.fill_(1.0)
-                assert launch((a.cuda_event, b.cuda_event)) == 0
+                assert launch((a.handle, b.handle)) == 0
             torch.cuda.synchronize()
-            return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+            return np.array([a.elapsed_ms(b) * 1e3 for a, b in evs])
 
         # warm up for a fixed time, not a count, so the clocks have ramped
         # after the host-side input generation whatever the kernel's length
@@ -800,15 +1046,11 @@ def time_shards():
                     assert launch() == 0
                 torch.cuda.synchronize()
             n = 30 if M * N * K > 1e11 else 100
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
             for a, b in evs:
-                a.record(st)
-                b.record(st)
+                assert launch((a.handle, b.handle)) == 0
             torch.cuda.synchronize()
-            for a, b in evs:
-                assert launch((a.cuda_event, b.cuda_event)) == 0
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            us = float(np.median([a.elapsed_ms(b) * 1e3 for a, b in evs]))
             t1 = us if g == 1 else t1
             tf = 2 * M * N * K / us / 1e6
             tile = binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16)
@@ -829,8 +1071,14 @@ def main():
         torch.backends.cuda.matmul.allow_tf32 = False
         time_configs()
         return
-    if args.counters_from:
-        counters_from(args.counters_from)
+    if args.counters_from or args.traffic_from:
+        counters_from(args.counters_from, args.traffic_from)
+        return
+    if args.trace_from:
+        trace_from(args.trace_from)
+        return
+    if args.counter_workloads:
+        counter_workloads()
         return
     if args.mfma_ceiling:
         mfma_ceiling()
@@ -843,9 +1091,6 @@ def main():
         return
     if args.activation:
         time_activation()
-        return
-    if args.traffic_from:
-        traffic_from(args.traffic_from)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -909,20 +1154,25 @@ def main():
             if events is not None and i in which:
                 # the library records the pair at the kernel's own start and end
                 e0, e1 = events[i]
-                st = L["fn"](*L["args"], binding.opts(-1, *L["ws"], e0.cuda_event, e1.cuda_event), sp)
+                st = L["fn"](*L["args"], binding.opts(-1, *L["ws"], e0.handle, e1.handle), sp)
             else:
                 st = L["fn"](*L["args"], L["plain"], sp)
             if st != 0:
                 raise RuntimeError(f"{L['name']}: {binding.status_string(st)}")
 
     def new_events(n):
-        evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                for _ in launches] for _ in range(n)]
-        for row in evs:  # create the underlying HIP events
-            for pair in row:
-                for e in pair:
-                    e.record(stream)
-        return evs
+        # the library's timing events: recording them writes back and
+        # invalidates no caches, so the timed kernel and the launches after
+        # it run as they do untimed
+        return [[[binding.TimingEvent(), binding.TimingEvent()] for _ in launches] for _ in range(n)]
+
+    # The events of the timed region and of the per-kernel pass are made
+    # first: making thousands of them takes the host milliseconds, during
+    # which the GPU would idle and its clock drop just before the timed steps.
+    ev = new_events(args.steps)
+    nb = min(args.steps, 50)
+    evb = new_events(nb)
+    torch.cuda.synchronize()
 
     # Time-based pre-warm, then the counted warm-up.  After the host has spent
     # seconds generating inputs the engine clock starts low and ramps within
@@ -940,18 +1190,14 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: whole steps, events around the dominant kernel only
-    ev = new_events(args.steps)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(ev[s], (dom_idx,))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = [ev[s][dom_idx][0].elapsed_time(ev[s][dom_idx][1]) for s in range(args.steps)]
+    dom_ms = [ev[s][dom_idx][0].elapsed_ms(ev[s][dom_idx][1]) for s in range(args.steps)]
 
     # per-kernel breakdown (not timed as steps): events around every launch
-    nb = min(args.steps, 50)
-    evb = new_events(nb)
     for s in range(nb):
         step(evb[s], range(len(launches)))
     torch.cuda.synchronize()
@@ -960,7 +1206,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     kernels = {}
     for i, L in enumerate(launches):
-        ms = [evb[s][i][0].elapsed_time(evb[s][i][1]) for s in range(nb)]
+        ms = [evb[s][i][0].elapsed_ms(evb[s][i][1]) for s in range(nb)]
         avg_us = float(np.mean(ms)) * 1e3
         kernels[L["name"]] = {
             "M": L["M"], "K": L["K"], "N": L["N"], "w": "f16" if L["w16"] else "f32",
@@ -1017,7 +1263,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "kernels_note": "per-kernel HIP-event durations (recorded by the launch at kernel start and end) "
+        "kernels_note": "per-kernel HIP-event durations (the library's timing events, recorded by the launch "
+                        "at kernel start and end) "
                         f"from a separate pass of {min(args.steps, 50)} steps",
     }
     print(json.dumps(line), flush=True)

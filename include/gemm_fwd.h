@@ -154,6 +154,29 @@ int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const 
                        int64_t M, int64_t K, int64_t N, int w_dtype, const gemm_opts *opts, void *stream);
 
 /*
+ * Timing events for gemm_opts.start_event / stop_event (measurement support,
+ * no operation of the pages): HIP events created with
+ * hipEventDisableSystemFence.  Recording a default timing event at a
+ * kernel's end writes back and invalidates the GPU caches at system scope,
+ * which lengthens the timed kernel and holds up the launches after it; these
+ * events record the kernel's start and end times without that.  They serve
+ * timing only: read them with gemm_timing_elapsed_ms once the stream or the
+ * device has been synchronised, never to order work or to make results
+ * visible to the host.  The caller owns each event and destroys it with
+ * gemm_timing_event_destroy.
+ *   gemm_timing_event_create   GEMM_ERR_NULL for a NULL `event`,
+ *                              GEMM_ERR_LAUNCH when the runtime refuses.
+ *   gemm_timing_elapsed_ms     *ms = stop - start in milliseconds;
+ *                              GEMM_ERR_NULL for a NULL argument,
+ *                              GEMM_ERR_LAUNCH when either event has not been
+ *                              recorded or has not completed.
+ *   gemm_timing_event_destroy  GEMM_ERR_LAUNCH when the runtime refuses.
+ */
+int gemm_timing_event_create(void **event);
+int gemm_timing_elapsed_ms(void *start, void *stop, float *ms);
+int gemm_timing_event_destroy(void *event);
+
+/*
  * For callers that cannot allocate device memory or hand in a workspace
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): gemm_fwd_swiglu_ex with the library's choice and a workspace

@@ -175,3 +175,41 @@ def test_event_options_match_and_record(swiglu):
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
     assert e0.elapsed_time(e1) > 0.0
     check(c, y1.cpu().numpy(), label="events")
+
+
+def test_timing_events():
+    """The library's timing events (no system-scope fence when recorded):
+    recorded by a launch at the kernel's start and end, they give a positive
+    time no longer than a torch event pair around the same launch; the
+    results are those of the plain entry point; NULL arguments are refused."""
+    import ctypes
+
+    import torch
+    b = _lib()
+    lib = b.load_library()
+    M, K, N = 512, 768, 768
+    c = inputs.random_case(12, M, K, N, residual=True)
+    X, W, R = to_dev(c["X"]), to_dev(c["W"]), to_dev(c["R"])
+    y0 = torch.empty((M, N), device=device())
+    y1 = torch.full((M, N), float("nan"), device=device())
+    st = torch.cuda.current_stream()
+    a = (X.data_ptr(), W.data_ptr(), R.data_ptr())
+    assert lib.gemm_fwd(*a, y0.data_ptr(), M, K, N, 0, st.cuda_stream) == 0
+    say("timing events around 512x768x768")
+    for _ in range(3):
+        t0, t1 = b.TimingEvent(), b.TimingEvent()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        assert lib.gemm_fwd_ex(*a, y1.data_ptr(), M, K, N, 0, b.opts(-1, None, 0, t0.handle, t1.handle),
+                               st.cuda_stream) == 0
+        e1.record(st)
+        torch.cuda.synchronize()
+        kernel_ms, outer_ms = t0.elapsed_ms(t1), e0.elapsed_time(e1)
+        say(f"  kernel {kernel_ms * 1e3:.2f} us, torch events around the launch {outer_ms * 1e3:.2f} us")
+        assert 0.0 < kernel_ms <= outer_ms * 1.01
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    assert lib.gemm_timing_event_create(None) == -1
+    ms = ctypes.c_float()
+    assert lib.gemm_timing_elapsed_ms(None, t1.handle, ctypes.byref(ms)) == -1
+    assert lib.gemm_timing_elapsed_ms(t0.handle, t1.handle, None) == -1
+    assert lib.gemm_timing_event_destroy(None) == 0

@@ -28,7 +28,7 @@ EXPORTED = (
     "gemm_matmul_at_swiglu_a_ex", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
     "gemm_bwd_workspace_bytes", "gemm_matmul_t_swiglu_bwd", "gemm_matmul_t_swiglu_bwd_ex",
     "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward",
-    "act_gelu_inplace",
+    "act_gelu_inplace", "gemm_timing_event_create", "gemm_timing_elapsed_ms", "gemm_timing_event_destroy",
 )
 
 
@@ -128,7 +128,39 @@ def _open(path):
     lib.act_ffn_gelu_backward.restype = c_int
     lib.act_gelu_inplace.argtypes = [p, p, i64, p]
     lib.act_gelu_inplace.restype = c_int
+    lib.gemm_timing_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.gemm_timing_event_create.restype = c_int
+    lib.gemm_timing_elapsed_ms.argtypes = [p, p, ctypes.POINTER(f32)]
+    lib.gemm_timing_elapsed_ms.restype = c_int
+    lib.gemm_timing_event_destroy.argtypes = [p]
+    lib.gemm_timing_event_destroy.restype = c_int
     return lib
+
+
+class TimingEvent:
+    """A timing event of the library (gemm_timing_event_create: no
+    system-scope cache writeback when it is recorded) for the start_event /
+    stop_event of gemm_opts; `handle` is what opts() takes."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        st = load_library().gemm_timing_event_create(ctypes.byref(h))
+        if st != 0:
+            raise GemmError(st, "gemm_timing_event_create")
+        self.handle = h.value
+
+    def elapsed_ms(self, stop: "TimingEvent") -> float:
+        """Milliseconds from this event to `stop` (both recorded and complete)."""
+        ms = ctypes.c_float()
+        st = load_library().gemm_timing_elapsed_ms(self.handle, stop.handle, ctypes.byref(ms))
+        if st != 0:
+            raise GemmError(st, "gemm_timing_elapsed_ms")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.gemm_timing_event_destroy(self.handle)
+            self.handle = None
 
 
 def status_string(status: int) -> str:

@@ -1600,6 +1600,35 @@ int gemm_select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w_f16, i
     return select_config(M, K, N, swiglu, w_f16, with_workspace != 0);
 }
 
+int gemm_timing_event_create(void **event) {
+    if (event == nullptr) return GEMM_ERR_NULL;
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_LAUNCH;
+    }
+    *event = e;
+    return GEMM_OK;
+}
+
+int gemm_timing_elapsed_ms(void *start, void *stop, float *ms) {
+    if (start == nullptr || stop == nullptr || ms == nullptr) return GEMM_ERR_NULL;
+    if (hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_LAUNCH;
+    }
+    return GEMM_OK;
+}
+
+int gemm_timing_event_destroy(void *event) {
+    if (event == nullptr) return GEMM_OK;
+    if (hipEventDestroy(static_cast<hipEvent_t>(event)) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_LAUNCH;
+    }
+    return GEMM_OK;
+}
+
 const char *gemm_status_string(int status) {
     switch (status) {
         case GEMM_OK: return "ok";
