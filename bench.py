@@ -35,9 +35,10 @@ HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
 this script (FETCH_SIZE, then WRITE_SIZE) and two of its --copy-calibration
 mode (a plain device copy of a known size), turned into bytes per launch by
 --traffic-from (for every kernel of the step) and kept in
-profiles/lm_head_traffic.json together with the hash of the kernel source
-they were taken on; the bench line reports them only while that hash still
-matches.
+profiles/lm_head_traffic.json together with the hash of the kernel's device
+code (and of the lm_head tile's table entry) they were taken on; the bench
+line reports them only while that hash still matches and the library still
+picks that tile.
 """
 from __future__ import annotations
 
@@ -645,7 +646,7 @@ def traffic_table(base, set_name):
         f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE = {copy_kib('copy_fetch') / 1024:.0f} MiB "
         f"and WRITE_SIZE = {copy_kib('copy_write') / 1024:.0f} MiB per dispatch, so FETCH_SIZE is scaled by "
         f"{f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.  Averages over every launch of each kernel; "
-        f"kernel source hash at measurement: {kernel_hash()}.",
+        f"hash of the kernels' device code and the lm_head tile's entry at measurement: {kernel_hash()}.",
         "",
         "Algorithmic bytes: A (G and U with SwiGLU) and W read once, R read once, Y written once.",
         "",
@@ -691,7 +692,7 @@ def counters_from(counters_base, traffic_base=None, out_dir=PROFILES):
             if set_name == "step":
                 lm = per["lm_head"]
                 out = {"kernel_sha256_16": kernel_hash(), "kernel": "lm_head (matmul_w16 512x768x16384)",
-                       "bytes_per_launch": lm["fetch_bytes"] + lm["write_bytes"], **lm}
+                       "tile": LM_HEAD_TILE, "bytes_per_launch": lm["fetch_bytes"] + lm["write_bytes"], **lm}
                 with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
                     json.dump(out, f, indent=1)
                     f.write("\n")
@@ -731,7 +732,7 @@ def trace_from(base, out_dir=PROFILES):
         f"    {cmd} > $R/gpurun_out/profiles/bench.log",
         "    python3 bench.py --trace-from gpurun_out/profiles      # writes this file",
         "",
-        f"Kernel source hash {kernel_hash()}.  The run made {pre} time-based pre-warm steps, {warm} counted warm-up "
+        f"Device-code hash {kernel_hash()}.  The run made {pre} time-based pre-warm steps, {warm} counted warm-up "
         f"steps, the {steps} timed steps and a pass of {nb} steps with events on every launch: "
         f"{len(rows)} GEMM launches in all.",
         "",
@@ -773,12 +774,20 @@ def trace_from(base, out_dir=PROFILES):
     print("\n".join(lines))
 
 
-def kernel_hash():
-    """Hash of the kernel source with comments and blank space removed, so
-    that only a change of code makes stored counter results stale."""
+LM_HEAD_TILE = "128x128x32_w2x2_sp4_pf3_il_dA"
+
+
+def kernel_hash(tile=LM_HEAD_TILE):
+    """Hash of the device code of the kernel source (everything before its
+    configuration table) and of `tile`'s entry in that table, with comments
+    and blank space removed, so that only a change to that kernel's code
+    makes stored counter results stale."""
     import re
     with open(KERNEL_SRC) as f:
         src = f.read()
+    cut = src.index("// configuration table")
+    entry = next(line for line in src[cut:].splitlines() if f'"{tile}"' in line)
+    src = src[:cut] + "\n" + entry
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
@@ -1223,7 +1232,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("kernel_sha256_16") == kernel_hash():
+        if t.get("kernel_sha256_16") == kernel_hash() and t.get("tile") == dom["config"] == LM_HEAD_TILE:
             traffic = t.get("bytes_per_launch")
     achieved = dom["flops"] / dom_avg_us / 1e6
     roofline = {

@@ -95,8 +95,9 @@ def test_config_table(lib):
     assert pick(8192, 3072, 768, 1, 1) == "64x384x32_w1x4_sp8_pf4_il"
     assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # without a workspace the long-K small grid does not split K
-    assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x64_k4_sp8_pf3_il"
-    assert pick(512, 3072, 768, 0, 0) == "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
+    assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"
+    assert pick(512, 3072, 768, 0, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"
+    assert pick(512, 3072, 768, 0, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"
     # mid-size grids: 128 x 64 while it gives two tiles per CU, 64 x 64 when
     # it fills one whole round and 64 x 48 does not
     assert pick(512, 768, 8192, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"

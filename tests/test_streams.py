@@ -7,7 +7,8 @@ buffer per stream).  Here:
   * split-K calls queued on six streams at once, each stream with its own
     workspace, all match the oracle;
   * at every shape where the library's choice splits K (the 512 x 3072 x 768
-    SwiGLU down-projection, the lm_head's input gradient 512 x 768 x 16384),
+    down-projection with SwiGLU and with a plain A, the lm_head's input
+    gradient 512 x 768 x 16384),
     the choice without a workspace matches the oracle on every element and
     is bitwise reproducible, and so is the split-K choice;
   * an explicit split-K configuration without a workspace is refused before
@@ -52,27 +53,33 @@ def test_split_k_calls_on_concurrent_streams():
         assert res["fails"] == 0, (i, res)
 
 
+@pytest.mark.parametrize("swiglu", [True, False])
 @pytest.mark.parametrize("use_workspace", [False, True])
-def test_swiglu_down_projection_with_and_without_workspace(use_workspace):
-    """512 x 3072 x 768 SwiGLU (the seq-512 down-projection, fp32 W): with a
-    workspace the library splits K in two, without one it takes the 16-row
-    tile over the whole K.  Both: every element against the oracle, and two
-    runs bitwise equal."""
+def test_long_k_small_grid_with_and_without_workspace(use_workspace, swiglu):
+    """512 x 3072 x 768 (the seq-512 down-projection, fp32 W), with SwiGLU
+    and with a plain A: with a workspace the library splits K in two, without
+    one it takes 16 x 96 tiles over the whole K.  Both: every element against
+    the oracle, and two runs bitwise equal."""
     import torch
     from tiled_dense_gemm_matmul_amd import binding
     c = inputs.cfg3()
-    d = {k: to_dev(c[k]) for k in ("G", "U", "W", "R")}
-    tile = binding.kernel_config(M, K, N, swiglu=True, workspace=use_workspace)
+    if not swiglu:
+        c = {"X": c["G"], "W": c["W"], "R": c["R"]}
+    d = {k: to_dev(v) for k, v in c.items()}
+    tile = binding.kernel_config(M, K, N, swiglu=swiglu, workspace=use_workspace)
     assert ("_ks" in tile) == use_workspace, tile
-    say(f"SwiGLU {M}x{K}x{N} workspace={use_workspace} tile {tile}")
+    say(f"{'SwiGLU' if swiglu else 'plain A'} {M}x{K}x{N} workspace={use_workspace} tile {tile}")
     ys = []
     for _ in range(2):
         y = torch.full((M, N), float("nan"), device=device())
-        binding.matmul_residual_swiglu_a(d["G"], d["U"], d["W"], d["R"], out=y, use_workspace=use_workspace)
+        if swiglu:
+            binding.matmul_residual_swiglu_a(d["G"], d["U"], d["W"], d["R"], out=y, use_workspace=use_workspace)
+        else:
+            binding.matmul(d["X"], d["W"], d["R"], out=y, use_workspace=use_workspace)
         torch.cuda.synchronize()
         ys.append(y.cpu().numpy())
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
-    ref, scale = oracle.gemm(c["G"], c["W"], R=c["R"], U=c["U"], want_scale=True)
+    ref, scale = oracle.gemm(c["G"] if swiglu else c["X"], c["W"], R=c["R"], U=c.get("U"), want_scale=True)
     res = oracle.compare(ys[0], ref, scale, oracle.TOL_W32)
     say(f"  max err/tol {res['max_ratio']:.3g} fails {res['fails']} of {res['n']}")
     assert res["fails"] == 0, res

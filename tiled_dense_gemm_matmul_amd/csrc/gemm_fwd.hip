@@ -978,8 +978,9 @@ constexpr ConfigEntry make_entry(const char *name) {
 }
 
 // Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL, PRIO, DMA>: the
-// tiles the library's own choice takes (select_config), then one of each
-// other kind of pipeline, so that every code path stays built and tested.
+// tiles the library's own forward choice takes (select_config), then one of
+// each other kind of pipeline, so that every code path stays built and
+// tested.
 const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x128x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 384, 32, 1, 4, 1, 8, 4, 1, 1>>("64x384x32_w1x4_sp8_pf4_il"),
@@ -987,10 +988,9 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
-    make_entry<Tile<32, 48, 64, 1, 1, 4, 4, 3, 1, 0, 1, 0, 2, 3>>("32x48x64_k4_sp4_pf3_dAW"),
     make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp4_pf2_dAW"),
-    make_entry<Tile<16, 96, 64, 1, 1, 4, 8, 3, 1, 1>>("16x96x64_k4_sp8_pf3_il"),
-    make_entry<Tile<32, 96, 64, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
+    make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 3, 1, 1, 1, 1, 2, 2>>("16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"),
+    make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 3>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
     // specialised, register staging only, two stages of loads in flight
@@ -1080,6 +1080,11 @@ int table_index(const ConfigEntry *table, int count, const char *name) {
 }
 int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, name); }
 
+bool same_name(const char *a, const char *b) {
+    while (*a && *a == *b) ++a, ++b;
+    return *a == 0 && *b == 0;
+}
+
 // Tile choice from the output grid, measured on MI355X: the largest tile
 // that still gives every CU work for the whole kernel, then narrower tiles
 // with the K range split over waves for small grids.  With SwiGLU, a
@@ -1098,55 +1103,51 @@ int config_index(const char *name) { return table_index(kConfigs, kNumConfigs, n
 // slices three at a time (8.2 against 9.8 with R), timed between the other
 // products of the seq-512 layer.
 // Long K on a small grid splits K over two workgroups when the caller
-// provides a workspace (`split`); the forward SwiGLU product then stages
-// 128-deep slices of K (512 x 3072 x 768: 26.5 against 26.9 us with 64).
+// provides a workspace (`split`), with 128-deep slices of K and, for a plain
+// A, LDS-destination loads of A too (512 x 3072 x 768: 26.0 us with SwiGLU;
+// 23.4 against 25.3 us with 64-deep slices for a plain A).  Without a
+// workspace, 16 x 96 tiles over the whole K, with 128-deep slices split over
+// two waves and W by LDS-destination loads: 26.6 against 39.2 us for 64-deep
+// slices split over four waves with SwiGLU, 25.7 against 34.7 for a plain A.
 // `forward` false: the rule as the backward products measured it, without
-// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep slices.
-int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward = true) {
-    (void)w16;
-    static const int big = config_index("128x128x32_w2x2_sp4_pf3_il_dA");
-    static const int swiglu_wide = config_index("64x384x32_w1x4_sp8_pf4_il");
-    static const int wide = config_index("128x192x32_w2x2_sp8_pf4_il");
-    static const int tall = config_index("128x64x32_w2x2_sp4_pf3_il_dA");
-    static const int mid = config_index("64x64x64_w2x2_sp4_dAW");
-    static const int narrow = config_index("64x48x64_w2x1_k2_sp4_pf3_il_dA");
-    static const int small = config_index("32x48x64_k4_sp4_pf3_dAW");
-    static const int small128 = config_index("32x48x128_k4_sp4_pf2_dAW");
-    static const int deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
-    static const int deep_split128 = config_index("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
-    static const int tiny = config_index("16x48x128_k4_sp4_dAW");
-    // a name missing from the table is a build error in spirit: report it
-    // as an unavailable configuration rather than run another one
-    static const bool complete = big >= 0 && swiglu_wide >= 0 && wide >= 0 && tall >= 0 && mid >= 0 &&
-                                 narrow >= 0 && small >= 0 && small128 >= 0 && deep >= 0 && deep_split >= 0 &&
-                                 deep_split128 >= 0 && tiny >= 0;
-    if (!complete) return -1;
+// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep slices;
+// every name it gives is in the backward table.
+const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split, bool forward) {
     const int64_t cus = 256;
-    if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return big;
-    if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return swiglu_wide;
+    if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
+    if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
-    if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return tall;
-    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return wide;
+    if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return "128x64x32_w2x2_sp4_pf3_il_dA";
+    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
-    if (t64 >= 2 * cus) return mid;
-    if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return mid;
-    if (t48 >= cus) return narrow;
-    if (M <= 128) return tiny;
+    if (t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
+    if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return "64x64x64_w2x2_sp4_dAW";
+    if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
+    if (M <= 128) return "16x48x128_k4_sp4_dAW";
     if (K >= 2048) {
         // long K on a small grid: split K in two when there is a workspace
         // (for outputs up to 2^19 elements, the range measured)
-        if (split && M * N <= kSplitMaxElems && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus)
-            return forward && swiglu ? deep_split128 : deep_split;
-        return deep;
+        if (split && M * N <= kSplitMaxElems && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus) {
+            if (!forward) return "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW";
+            return swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW";
+        }
+        return forward ? "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW" : "16x96x64_k4_sp8_pf3_il";
     }
-    return forward ? small128 : small;
+    return forward ? "32x48x128_k4_sp4_pf2_dAW" : "32x48x64_k4_sp4_pf3_dAW";
+}
+
+// The forward choice: an index into kConfigs (-1 if the rule names a tile
+// the table lacks, which would be a build error in spirit).
+int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split) {
+    (void)w16;
+    return config_index(select_rule(M, K, N, swiglu, split, true));
 }
 
 // Tile choice for the backward products, by their kernel dimensions (output
-// rows, contraction, output columns): the forward rule, with two exceptions
-// measured on the seq-512 model's backward shapes.  A transposed A is read
+// rows, contraction, output columns): the shared rule (select_rule with
+// `forward` false), with these exceptions measured on the seq-512 model's
+// backward shapes.  A transposed A is read
 // with four LDS reads per fragment, so with a short contraction the 64 x 64
 // tiles lose to 32 x 48 tiles with the K range split over four waves (about
 // 20% at 768 x 512 x 3072 and 3072 x 512 x 768).  With a transposed B and a
@@ -1169,42 +1170,36 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // at 768 x 16384 x 3072 (with ragged 48-row tiles, 1024 x 8192 x 4096, they
 // lose 3%).  The split-K tiles need the caller's workspace (`split`).
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
-    static const int fwd_mid = config_index("64x64x64_w2x2_sp4_dAW");
-    static const int mid = table_index(kBwdConfigs, kNumBwdConfigs, "64x64x64_w2x2_sp4");
-    static const int fwd_deep = config_index("16x96x64_k4_sp8_pf3_il");
-    static const int fwd_deep_split = config_index("32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW");
-    static const int small = table_index(kBwdConfigs, kNumBwdConfigs, "32x48x64_k4_sp4_pf3_dAW");
-    static const int tiny = table_index(kBwdConfigs, kNumBwdConfigs, "16x48x128_k4_sp4_dAW");
-    static const int long_k = table_index(kBwdConfigs, kNumBwdConfigs, "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
-    static const int square = table_index(kBwdConfigs, kNumBwdConfigs, "48x48x64_k4_sp4_pf3_dAW");
-    static const int tall = table_index(kBwdConfigs, kNumBwdConfigs, "128x64x32_w2x2_sp4_pf3_il_dA");
-    static const int swiglu_sq = table_index(kBwdConfigs, kNumBwdConfigs, "96x96x64_w2x2_sp4_pf3_il_dA");
+    static const char *const fwd_mid = "64x64x64_w2x2_sp4_dAW", *const mid = "64x64x64_w2x2_sp4";
+    static const char *const deep = "16x96x64_k4_sp8_pf3_il";
+    static const char *const deep_split = "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW";
+    static const char *const small = "32x48x64_k4_sp4_pf3_dAW";
+    auto bwd = [](const char *name) { return table_index(kBwdConfigs, kNumBwdConfigs, name); };
     const int64_t cus = 256;
-    // the forward rule without its SwiGLU and forward-only tiles, which the
+    // the shared rule without its SwiGLU and forward-only tiles, which the
     // backward table does not hold
-    const int f = select_config(M, K, N, 0, 0, split, false);
-    if (f < 0) return -1;
+    const char *f = select_rule(M, K, N, 0, split, false);
     if (op == kOpNT && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus && ceil_div(M, 128) * ceil_div(N, 128) < 2 * cus)
-        return tall;
-    // without split-K the forward rule's long-K choice is the deep tile
-    const bool long_k_grid = f == fwd_deep_split || (!split && f == fwd_deep);
-    if (op == kOpNT && long_k_grid && K <= 4096) return tiny;
-    if (split && op == kOpNT && f == fwd_deep_split && K >= 8192 && M * N <= kSplitMaxElems &&
+        return bwd("128x64x32_w2x2_sp4_pf3_il_dA");
+    // without split-K the rule's long-K choice is the deep tile
+    const bool long_k_grid = same_name(f, deep_split) || (!split && same_name(f, deep));
+    if (op == kOpNT && long_k_grid && K <= 4096) return bwd("16x48x128_k4_sp4_dAW");
+    if (split && op == kOpNT && same_name(f, deep_split) && K >= 8192 && M * N <= kSplitMaxElems &&
         ceil_div(M, 128) * ceil_div(N, 96) * 8 >= 128)
-        return long_k;
-    // a transposed A takes 32 x 48 tiles where the forward rule takes 64 x 64
+        return bwd("128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA");
+    // a transposed A takes 32 x 48 tiles where the rule takes 64 x 64
     // (whose backward form stages with registers)
-    const int r = f == fwd_mid ? (op == kOpTN ? small : mid)
-                               : table_index(kBwdConfigs, kNumBwdConfigs, kConfigs[f].name);
-    if (op == kOpTN && swiglu && r == small && K >= 4096 && ceil_div(M, 96) * ceil_div(N, 96) >= cus)
-        return swiglu_sq;
-    if (op == kOpTN && (r == small || f == fwd_deep)) {
+    const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
+    if (op == kOpTN && swiglu && same_name(r, small) && K >= 4096 && ceil_div(M, 96) * ceil_div(N, 96) >= cus)
+        return bwd("96x96x64_w2x2_sp4_pf3_il_dA");
+    if (op == kOpTN && (same_name(r, small) || same_name(f, deep))) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
-        if (t32 > cus && t32 < 2 * cus && t48 <= cus) return square;
+        if (t32 > cus && t32 < 2 * cus && t48 <= cus) return bwd("48x48x64_k4_sp4_pf3_dAW");
         // long contractions whose output splits into whole 48 x 48 tiles
-        if (r == small && K >= 4096 && M % 48 == 0 && N % 48 == 0 && t48 >= cus) return square;
+        if (same_name(r, small) && K >= 4096 && M % 48 == 0 && N % 48 == 0 && t48 >= cus)
+            return bwd("48x48x64_k4_sp4_pf3_dAW");
     }
-    return r;
+    return bwd(r);
 }
 
 // ---------------------------------------------------------------------------
