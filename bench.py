@@ -889,6 +889,26 @@ CONFIGS = [
 ]
 
 
+def queued_launch_times(launch, n, between=None):
+    """Durations (us) of n launches, each timed by the library's timing
+    events, all queued behind a spin kernel of a few milliseconds so that the
+    GPU runs them back to back: a short kernel whose launch reaches an idle
+    GPU (the host enqueueing slower than the kernel runs) measures about one
+    dispatch latency (~4 us) longer.  `between` enqueues work before each
+    launch (outside its events)."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
+    torch.cuda._sleep(10_000_000)
+    for a, b in evs:
+        if between is not None:
+            between()
+        assert launch((a.handle, b.handle)) == 0
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_ms(b) * 1e3 for a, b in evs])
+
+
 def time_configs():
     """Each workload configuration on its own, timed per launch by events
     that the launch records at the kernel's start and end.  Warm: back-to-
@@ -939,14 +959,8 @@ def time_configs():
 
         def sample(n, flush_between):
             """n launches queued back to back (a flush kernel between them
-            when cold), each timed by its own event pair; read at the end."""
-            evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
-            for a, b in evs:
-                if flush_between:
-                    flush.fill_(1.0)
-                assert launch((a.handle, b.handle)) == 0
-            torch.cuda.synchronize()
-            return np.array([a.elapsed_ms(b) * 1e3 for a, b in evs])
+            when cold), each timed by its own event pair."""
+            return queued_launch_times(launch, n, (lambda: flush.fill_(1.0)) if flush_between else None)
 
         # warm up for a fixed time, not a count, so the clocks have ramped
         # after the host-side input generation whatever the kernel's length
@@ -1055,11 +1069,7 @@ def time_shards():
                     assert launch() == 0
                 torch.cuda.synchronize()
             n = 30 if M * N * K > 1e11 else 100
-            evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
-            for a, b in evs:
-                assert launch((a.handle, b.handle)) == 0
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_ms(b) * 1e3 for a, b in evs]))
+            us = float(np.median(queued_launch_times(launch, n)))
             t1 = us if g == 1 else t1
             tf = 2 * M * N * K / us / 1e6
             tile = binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16)

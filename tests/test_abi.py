@@ -88,7 +88,7 @@ def test_config_table(lib):
         return lib.gemm_config_name(lib.gemm_select_config(M, K, N, sw, w16, ws)).decode()
     # the workload configurations (their tiles are the ones bench.py times)
     assert pick(128, 768, 768, 0, 0) == "16x48x128_k4_sp4_dAW"
-    assert pick(512, 768, 768, 0, 0) == "32x48x128_k4_sp4_pf2_dAW"
+    assert pick(512, 768, 768, 0, 0) == "32x48x128_k4_sp8_pf2_dAW"
     assert pick(512, 3072, 768, 1, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
     assert pick(512, 768, 16384, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert pick(512, 768, 3072, 0, 1) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"

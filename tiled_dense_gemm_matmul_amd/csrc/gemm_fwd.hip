@@ -988,7 +988,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
-    make_entry<Tile<32, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp4_pf2_dAW"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp8_pf2_dAW"),
     make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 3, 1, 1, 1, 1, 2, 2>>("16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 3>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
@@ -1098,10 +1098,13 @@ bool same_name(const char *a, const char *b) {
 // than 128 x 192 on the shapes measured.  And 64 x 64 tiles
 // rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
 // and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
-// The smallest forward grids stage 128-deep slices of K two at a time: at
-// 512 x 768 x 768, one 32 x 48 tile per CU, 7.9 against 9.4 us with 64-deep
-// slices three at a time (8.2 against 9.8 with R), timed between the other
-// products of the seq-512 layer.
+// The smallest forward grids stage 128-deep slices of K two at a time with
+// eight staging waves: at 512 x 768 x 768, one 32 x 48 tile per CU, 7.6
+// against 9.3 us with 64-deep slices three at a time and four staging waves
+// (8.1 against 9.7 with R), timed between the other products of the seq-512
+// layer; 16.1 against 17.5 us at 512 x 1536 x 768 with SwiGLU and 12.5
+// against 16.1 without (one shape measured the other way: 512 x 1024 x 1024
+// with f16 W, 18.7 against 17.2 us).
 // Long K on a small grid splits K over two workgroups when the caller
 // provides a workspace (`split`), with 128-deep slices of K and, for a plain
 // A, LDS-destination loads of A too (512 x 3072 x 768: 26.0 us with SwiGLU;
@@ -1134,7 +1137,7 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split,
         }
         return forward ? "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW" : "16x96x64_k4_sp8_pf3_il";
     }
-    return forward ? "32x48x128_k4_sp4_pf2_dAW" : "32x48x64_k4_sp4_pf3_dAW";
+    return forward ? "32x48x128_k4_sp8_pf2_dAW" : "32x48x64_k4_sp4_pf3_dAW";
 }
 
 // The forward choice: an index into kConfigs (-1 if the rule names a tile
