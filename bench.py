@@ -146,14 +146,14 @@ BACKWARD = [
 
 def time_backward():
     """The backward products at the seq-512 model's shapes, each on its own:
-    batches of back-to-back launches between two events (so the figure
-    includes the launch gaps), after at least 0.2 s of warm-up; torch.matmul
-    in fp32 on the same plain product as context."""
+    batches of back-to-back launches queued behind busy_blocker(), between two
+    timing-event markers (so the figure includes the launch gaps), after at
+    least 0.2 s of warm-up; torch.matmul in fp32 on the same plain product as
+    context."""
     import numpy as np
     import torch
     from tiled_dense_gemm_matmul_amd import binding, inputs
     dev = torch.device("cuda:0")
-    st = torch.cuda.current_stream(dev)
     rows = []
     lines = ["| product | kernel | M×K×N (forward names) | output | µs per launch | TFLOP/s | % of 157.3 | "
              "torch.matmul fp32 µs |", "|---|---|---|---|---|---|---|---|"]
@@ -176,15 +176,7 @@ def time_backward():
                 ref = lambda: torch.matmul(t["X"].t(), t["dY"])
             kcfg = binding.bwd_kernel_config("matmul_at", M, K, N, swiglu="swiglu" in op)
 
-        def batch(fn, n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(n):
-                fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / n
-
+        batch = batch_time
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.2:
             batch(run, 10)
@@ -225,13 +217,7 @@ def time_backward():
         while time.perf_counter() - t0 < 0.2:
             fn()
             torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(50):
-            fn()
-        e1.record(st)
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) * 1e3 / 50
+        res[name] = batch_time(fn, 50)
     print(json.dumps({"ffn_down_dH_and_swiglu_backward_us": {k: round(v, 2) for k, v in res.items()}}),
           file=sys.stderr, flush=True)
     lines += ["", f"FFN down-projection input gradient + SwiGLU backward ({M}×{K}×{N}): matmul_t then "
@@ -242,8 +228,9 @@ def time_backward():
 
 
 def time_loss():
-    """cross_entropy over the lm_head logits, each launch timed by its own
-    event pair (median of the launches), warm (logits of the seq-512 step fit
+    """cross_entropy over the lm_head logits, each launch between its own
+    pair of timing-event markers (median of the launches, all queued behind
+    busy_blocker()), warm (logits of the seq-512 step fit
     the 256 MB Infinity Cache) and cold (a 512 MiB buffer written between
     launches).  The kernel rewrites the logits in place, so later launches
     see gradients rather than logits; the work does not depend on the values.
@@ -270,15 +257,7 @@ def time_loss():
                                              inv, st.cuda_stream)
 
         def sample(n, cold):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            for a, b in evs:
-                if cold:
-                    flush.fill_(1.0)
-                a.record(st)
-                run()
-                b.record(st)
-            torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            return float(np.median(marker_times(run, n, (lambda: flush.fill_(1.0)) if cold else None)))
 
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.2:
@@ -287,13 +266,7 @@ def time_loss():
         n = 50 if S * V < 1e8 else 10
         warm, cold = sample(n, False), sample(n, True)
         total = torch.empty(1, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(20):
-            lib.loss_sum_losses(losses.data_ptr(), total.data_ptr(), S, st.cuda_stream)
-        e1.record(st)
-        torch.cuda.synchronize()
-        sl_us = e0.elapsed_time(e1) * 1e3 / 20
+        sl_us = batch_time(lambda: lib.loss_sum_losses(losses.data_ptr(), total.data_ptr(), S, st.cuda_stream), 20)
         nbytes = 2 * S * V * 4 + 2 * S * 4
         path = "registers, 256 threads/row" if V <= 16384 else ("registers, 1024 threads/row" if V <= 65536
                                                                  else "streaming")
@@ -311,8 +284,9 @@ def time_loss():
 
 
 def time_activation():
-    """The FFN activation kernels on their own, each launch timed by its own
-    event pair around the C entry point (median), warm and cold (a 512 MiB
+    """The FFN activation kernels on their own, each launch between its own
+    pair of timing-event markers around the C entry point (median, all queued
+    behind busy_blocker()), warm and cold (a 512 MiB
     buffer written between launches).  Algorithmic bytes per element:
     ffn_swiglu_backward reads three arrays and writes two (20 B),
     ffn_gelu_backward reads two and writes one (12 B), gelu_inplace reads
@@ -341,15 +315,7 @@ def time_activation():
         ]
         for name, bpe, run in kernels:
             def sample(k, cold):
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
-                for a, b in evs:
-                    if cold:
-                        flush.fill_(1.0)
-                    a.record(st)
-                    assert run() == 0
-                    b.record(st)
-                torch.cuda.synchronize()
-                return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+                return float(np.median(marker_times(run, k, (lambda: flush.fill_(1.0)) if cold else None)))
             t0 = time.perf_counter()
             while time.perf_counter() - t0 < 0.2:
                 run()
@@ -889,18 +855,75 @@ CONFIGS = [
 ]
 
 
+_BLOCKER = []
+
+
+def busy_blocker():
+    """Queue a few milliseconds of real work (three 4096^3 fp32 products in
+    torch) ahead of the launches to be timed, so that the host has enqueued
+    them all before the first one runs and the GPU runs them back to back.
+    A spin kernel would do the first part, but it leaves the GPU idle for
+    those milliseconds, the engine clock drops, and the kernels after it run
+    up to 12% slow until it has ramped again."""
+    import torch
+    if not _BLOCKER:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn((4096, 4096), device="cuda", generator=g)
+        _BLOCKER.extend([a, a.clone(), torch.empty_like(a)])
+    a, b, c = _BLOCKER
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+
+
+def marker_times(run, n, between=None):
+    """Durations (us) of n calls of `run` (a launch that records no events
+    itself), each between two of the library's timing events recorded as
+    markers, all queued behind busy_blocker() so that the GPU runs them back
+    to back.  `between` enqueues work before each marker pair."""
+    import numpy as np
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    st = torch.cuda.current_stream()
+    evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
+    busy_blocker()
+    for a, b in evs:
+        if between is not None:
+            between()
+        a.record(st)
+        assert run() in (0, None)
+        b.record(st)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_ms(b) * 1e3 for a, b in evs])
+
+
+def batch_time(fn, n):
+    """Microseconds per call of n calls of `fn` queued back to back behind
+    busy_blocker(), between two timing-event markers (launch gaps included)."""
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    st = torch.cuda.current_stream()
+    e0, e1 = binding.TimingEvent(), binding.TimingEvent()
+    busy_blocker()
+    e0.record(st)
+    for _ in range(n):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) * 1e3 / n
+
+
 def queued_launch_times(launch, n, between=None):
     """Durations (us) of n launches, each timed by the library's timing
-    events, all queued behind a spin kernel of a few milliseconds so that the
-    GPU runs them back to back: a short kernel whose launch reaches an idle
-    GPU (the host enqueueing slower than the kernel runs) measures about one
-    dispatch latency (~4 us) longer.  `between` enqueues work before each
-    launch (outside its events)."""
+    events, all queued behind busy_blocker() so that the GPU runs them back
+    to back: a short kernel whose launch reaches an idle GPU (the host
+    enqueueing slower than the kernel runs) measures about one dispatch
+    latency (~4 us) longer.  `between` enqueues work before each launch
+    (outside its events)."""
     import numpy as np
     import torch
     from tiled_dense_gemm_matmul_amd import binding
     evs = [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
-    torch.cuda._sleep(10_000_000)
+    busy_blocker()
     for a, b in evs:
         if between is not None:
             between()

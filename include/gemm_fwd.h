@@ -170,9 +170,15 @@ int gemm_fwd_swiglu_ex(const float *GATE, const float *UP, const void *W, const 
  *                              GEMM_ERR_NULL for a NULL argument,
  *                              GEMM_ERR_LAUNCH when either event has not been
  *                              recorded or has not completed.
+ *   gemm_timing_event_record   records the event on `stream` (hipStream_t,
+ *                              NULL for the null stream) as a marker between
+ *                              launches, for entry points that take no
+ *                              events; GEMM_ERR_NULL for a NULL `event`,
+ *                              GEMM_ERR_LAUNCH when the runtime refuses.
  *   gemm_timing_event_destroy  GEMM_ERR_LAUNCH when the runtime refuses.
  */
 int gemm_timing_event_create(void **event);
+int gemm_timing_event_record(void *event, void *stream);
 int gemm_timing_elapsed_ms(void *start, void *stop, float *ms);
 int gemm_timing_event_destroy(void *event);
 

@@ -180,8 +180,9 @@ def test_event_options_match_and_record(swiglu):
 def test_timing_events():
     """The library's timing events (no system-scope fence when recorded):
     recorded by a launch at the kernel's start and end, they give a positive
-    time no longer than a torch event pair around the same launch; the
-    results are those of the plain entry point; NULL arguments are refused."""
+    time no longer than a torch event pair around the same launch; recorded
+    as markers around a launch, a positive time; the results are those of
+    the plain entry point; NULL arguments are refused."""
     import ctypes
 
     import torch
@@ -208,6 +209,14 @@ def test_timing_events():
         say(f"  kernel {kernel_ms * 1e3:.2f} us, torch events around the launch {outer_ms * 1e3:.2f} us")
         assert 0.0 < kernel_ms <= outer_ms * 1.01
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    # recorded as markers around a launch that records no events itself
+    m0, m1 = b.TimingEvent(), b.TimingEvent()
+    m0.record(st)
+    assert lib.gemm_fwd(*a, y1.data_ptr(), M, K, N, 0, st.cuda_stream) == 0
+    m1.record(st)
+    torch.cuda.synchronize()
+    assert m0.elapsed_ms(m1) > 0.0
+    assert lib.gemm_timing_event_record(None, st.cuda_stream) == -1
     assert lib.gemm_timing_event_create(None) == -1
     ms = ctypes.c_float()
     assert lib.gemm_timing_elapsed_ms(None, t1.handle, ctypes.byref(ms)) == -1

@@ -28,7 +28,8 @@ EXPORTED = (
     "gemm_matmul_at_swiglu_a_ex", "gemm_bwd_num_configs", "gemm_bwd_config_name", "gemm_bwd_select_config",
     "gemm_bwd_workspace_bytes", "gemm_matmul_t_swiglu_bwd", "gemm_matmul_t_swiglu_bwd_ex",
     "loss_cross_entropy", "loss_sum_losses", "act_ffn_swiglu_backward", "act_ffn_gelu_backward",
-    "act_gelu_inplace", "gemm_timing_event_create", "gemm_timing_elapsed_ms", "gemm_timing_event_destroy",
+    "act_gelu_inplace", "gemm_timing_event_create", "gemm_timing_event_record", "gemm_timing_elapsed_ms",
+    "gemm_timing_event_destroy",
 )
 
 
@@ -130,6 +131,8 @@ def _open(path):
     lib.act_gelu_inplace.restype = c_int
     lib.gemm_timing_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     lib.gemm_timing_event_create.restype = c_int
+    lib.gemm_timing_event_record.argtypes = [p, p]
+    lib.gemm_timing_event_record.restype = c_int
     lib.gemm_timing_elapsed_ms.argtypes = [p, p, ctypes.POINTER(f32)]
     lib.gemm_timing_elapsed_ms.restype = c_int
     lib.gemm_timing_event_destroy.argtypes = [p]
@@ -148,6 +151,16 @@ class TimingEvent:
         if st != 0:
             raise GemmError(st, "gemm_timing_event_create")
         self.handle = h.value
+
+    def record(self, stream=None) -> None:
+        """Record the event on `stream` (a torch stream or a raw handle;
+        None: torch's current stream) as a marker between launches."""
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        st = load_library().gemm_timing_event_record(self.handle, handle)
+        if st != 0:
+            raise GemmError(st, "gemm_timing_event_record")
 
     def elapsed_ms(self, stop: "TimingEvent") -> float:
         """Milliseconds from this event to `stop` (both recorded and complete)."""

@@ -1609,6 +1609,15 @@ int gemm_timing_event_create(void **event) {
     return GEMM_OK;
 }
 
+int gemm_timing_event_record(void *event, void *stream) {
+    if (event == nullptr) return GEMM_ERR_NULL;
+    if (hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_LAUNCH;
+    }
+    return GEMM_OK;
+}
+
 int gemm_timing_elapsed_ms(void *start, void *stop, float *ms) {
     if (start == nullptr || stop == nullptr || ms == nullptr) return GEMM_ERR_NULL;
     if (hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) != hipSuccess) {
