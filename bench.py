@@ -687,16 +687,17 @@ def trace_from(base, out_dir=PROFILES):
         return [dur[j] for j in range(lo, hi) if j % n == i]
 
     flops = {k: 2 * M * K * N for (k, M, K, N, *_r) in COUNTER_SETS["step"]["kernels"]}
-    cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/profiles/trace -o bench -- "
+    cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o bench -- "
            f"python3 $R/bench.py --steps {steps} --warmup {warm} --no-cpu")
     lines = [
         "# Kernel trace of the seq-512 forward step (bench.py)",
         "",
-        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host):",
+        "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root on the GPU host and $OUT an output "
+        "directory):",
         "",
-        "    python3 $R/bench.py > $R/gpurun_out/profiles/bench_plain.log      # unprofiled, for comparison",
-        f"    {cmd} > $R/gpurun_out/profiles/bench.log",
-        "    python3 bench.py --trace-from gpurun_out/profiles      # writes this file",
+        "    python3 $R/bench.py > $OUT/bench_plain.log      # unprofiled, for comparison",
+        f"    {cmd} > $OUT/bench.log",
+        "    python3 bench.py --trace-from $OUT      # writes this file",
         "",
         f"Device-code hash {kernel_hash()}.  The run made {pre} time-based pre-warm steps, {warm} counted warm-up "
         f"steps, the {steps} timed steps and a pass of {nb} steps with events on every launch: "

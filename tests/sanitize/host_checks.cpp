@@ -1,4 +1,4 @@
-// Driver for the library's host code built with AddressSanitizer and
+// Test program for the library's host code built with AddressSanitizer and
 // UndefinedBehaviorSanitizer (hipcc, instrumentation on the host side only):
 // every entry point's argument validation (each status code, extreme and
 // overflowing shapes, aliasing, workspace errors), and the tile-choice and

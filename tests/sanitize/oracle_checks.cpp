@@ -1,4 +1,4 @@
-// Driver for the oracle built with AddressSanitizer and UndefinedBehavior-
+// Test program for the oracle built with AddressSanitizer and UndefinedBehavior-
 // Sanitizer (host code, g++): brute-force integer products (all variants,
 // row subsets, binary16 weights), the binary16 decoder over every pattern,
 // row/column sums, and the argument checks.  Exits non-zero on a mismatch;

@@ -1,6 +1,6 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU).
 
-Two drivers under tests/sanitize/: the oracle built by g++ with both
+Two test programs under tests/sanitize/: the oracle built by g++ with both
 sanitizers (brute-force products in every variant, row subsets, binary16
 weights, the decoder over every pattern, row/column sums, argument checks),
 and the library's host code built by hipcc with the sanitizers on the host
@@ -49,13 +49,13 @@ def test_library_host_code_under_sanitizers():
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    driver = os.path.join(ROOT, "tests", "sanitize", "host_checks.cpp")
+    prog = os.path.join(ROOT, "tests", "sanitize", "host_checks.cpp")
     # instrumentation on the host side only: each -fsanitize= right after -Xarch_host
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=undefined"]
     cmd = [hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", *san, "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), *LIB_SRCS, driver]
-    exe = _cached_build("host_checks", cmd, LIB_SRCS + HEADERS + [driver])
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), *LIB_SRCS, prog]
+    exe = _cached_build("host_checks", cmd, LIB_SRCS + HEADERS + [prog])
     r = subprocess.run([exe], env=ENV, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "host checks ok" in r.stdout
