@@ -91,7 +91,7 @@ def test_config_table(lib):
     assert pick(512, 768, 768, 0, 0) == "32x48x128_k4_sp8_pf2_dAW"
     assert pick(512, 3072, 768, 1, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
     assert pick(512, 768, 16384, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
-    assert pick(512, 768, 3072, 0, 1) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert pick(512, 768, 3072, 0, 1) == "128x48x32_w2x1_k2_sp4_pf3_il_dA"
     assert pick(8192, 3072, 768, 1, 1) == "64x384x32_w1x4_sp8_pf4_il"
     assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # without a workspace the long-K small grid does not split K

@@ -1,6 +1,6 @@
 """Parity in the configurations that the tile-choice rules for mid-size and
 batch-size grids pick (each test first checks that the rule picked it):
-the forward 128 x 64 and 64 x 64 tiles, and the backward 128 x 64 (transposed
+the forward 128 x 64, 128 x 48 and 64 x 64 tiles, and the backward 128 x 64 (transposed
 B), 48 x 48 (long-contraction dW) and 96 x 96 (SwiGLU dW over a long
 contraction) tiles.  Large outputs are compared on sampled rows that include
 the last tile's rows."""
@@ -26,6 +26,8 @@ def _rows(M, seed, count=48, tail=128):
     (512, 768, 8192, True, False, "128x64x32_w2x2_sp4_pf3_il_dA"),
     (8192, 768, 768, False, True, "128x64x32_w2x2_sp4_pf3_il_dA"),
     (512, 768, 2048, True, False, "64x64x64_w2x2_sp4_dAW"),
+    (512, 768, 3072, True, False, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
+    (2048, 768, 772, False, True, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
 ])
 def test_forward_rule(M, K, N, w16, resid, tile):
     from tiled_dense_gemm_matmul_amd import binding

@@ -987,6 +987,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
+    make_entry<Tile<128, 48, 32, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("128x48x32_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp8_pf2_dAW"),
     make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 3, 1, 1, 1, 1, 2, 2>>("16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"),
@@ -1098,6 +1099,11 @@ bool same_name(const char *a, const char *b) {
 // than 128 x 192 on the shapes measured.  And 64 x 64 tiles
 // rather than 64 x 48 where the 64 x 64 grid is one whole round of the CUs
 // and the 64 x 48 one is not (512 x 768 x 2048: 17.8 against 21.8 us).
+// Where 128 x 48 tiles fill the CUs and larger ones do not, forward products
+// take them rather than 64 x 48 (two per CU): 21.7 against 22.0 us at
+// 512 x 768 x 3072 with f16 W, 32.9 against 36.2 at 1024 x 768 x 1536 and
+// 40.6 against 44.3 at 2048 x 1024 x 768 with SwiGLU, level (within 0.5%)
+// at 2048 x 768 x 768 and 512 x 1024 x 3072.
 // The smallest forward grids stage 128-deep slices of K two at a time with
 // eight staging waves: at 512 x 768 x 768, one 32 x 48 tile per CU, 7.6
 // against 9.3 us with 64-deep slices three at a time and four staging waves
@@ -1113,8 +1119,8 @@ bool same_name(const char *a, const char *b) {
 // two waves and W by LDS-destination loads: 26.6 against 39.2 us for 64-deep
 // slices split over four waves with SwiGLU, 25.7 against 34.7 for a plain A.
 // `forward` false: the rule as the backward products measured it, without
-// the 128 x 64 tile, the whole-round 64 x 64 choice and the 128-deep slices;
-// every name it gives is in the backward table.
+// the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice and the
+// 128-deep slices; every name it gives is in the backward table.
 const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split, bool forward) {
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
@@ -1126,6 +1132,9 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split,
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
     if (t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
     if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return "64x64x64_w2x2_sp4_dAW";
+    // forward products: 128 x 48 where that grid fills the CUs, which stages
+    // (and widens, or combines) each block of W (or A) half as often
+    if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
     if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
     if (M <= 128) return "16x48x128_k4_sp4_dAW";
     if (K >= 2048) {
