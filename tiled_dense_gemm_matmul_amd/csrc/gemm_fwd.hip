@@ -828,27 +828,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     // K-slice copies in the fixed order 0, 1, ..., WK-1, adds R, and stores
     // Y with 16-byte buffer accesses.  Lane (q4, r16) of a 16x16 MFMA tile
     // holds rows 4*q4 .. 4*q4+3 of column r16.
-    constexpr int Q = BN / 4;
-    constexpr int ITEMS = BM * Q;
-    constexpr int FIT = (ITEMS + NC - 1) / NC;  // float4 items per compute thread
-    const size_t tile_off = (size_t)m0 * N + n0;
-    // Without split-K, the residual's loads go out before the accumulators
-    // are parked, so their latency overlaps the reduction through LDS.
-    constexpr bool R_EARLY = RESID && KS == 1 && EPI == kEpiStore;
-    f32x4 r_early[R_EARLY ? FIT : 1];
-    if constexpr (R_EARLY) {
-        if (computes) {
-            const Rsrc rR = make_rsrc(p.R + tile_off, rows_valid * N * 4);
-#pragma unroll
-            for (int it = 0; it < FIT; ++it) {
-                const int idx = tid + it * NC;
-                if (ITEMS % NC != 0 && idx >= ITEMS) break;
-                const int row = idx / Q, c4 = idx % Q;
-                const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
-                r_early[it] = load_f32x4(rR, ok ? (row * N + c4 * 4) * 4 : kOOB);
-            }
-        }
-    }
     if (computes) {
         float *Ct = lds + wk * BM * CSTR;
 #pragma unroll
@@ -861,6 +840,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     }
     stage_barrier();
 
+    const size_t tile_off = (size_t)m0 * N + n0;
     // The last step of the epilogue for four consecutive outputs at byte
     // offset `off` of the tile (kOOB for masked items): store them (plus R),
     // or turn them into the two SwiGLU gradients.
@@ -877,11 +857,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                 store_f32x4(rY, off, dg);
                 store_f32x4(rY2, off, du);
             } else {
-                if constexpr (RESID && !R_EARLY) v += load_f32x4(rR, off);
+                if constexpr (RESID) v += load_f32x4(rR, off);
                 store_f32x4(rY, off, v);
             }
         };
     };
+    constexpr int Q = BN / 4;
+    constexpr int ITEMS = BM * Q;
     if constexpr (KS > 1) {
         // Publish this split's partial tile, then count the arrival.
         __shared__ int sk_last;
@@ -954,7 +936,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     const int ybytes = rows_valid * N * 4;
     const auto finish = make_finish(ybytes);
 #pragma unroll
-    for (int it = 0; it < FIT; ++it) {
+    for (int it = 0; it < (ITEMS + NC - 1) / NC; ++it) {
         const int idx = tid + it * NC;
         if (ITEMS % NC != 0 && idx >= ITEMS) break;
         const int row = idx / Q, c4 = idx % Q;
@@ -964,7 +946,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             v += *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * CSTR + c4 * 4);
         const bool ok = (m0 + row < M) && (n0 + c4 * 4 < N);
         const int off = ok ? (row * N + c4 * 4) * 4 : kOOB;
-        if constexpr (R_EARLY) v += r_early[it];
         finish(v, off);
     }
 }
