@@ -89,7 +89,8 @@ extern "C" {
 #define GEMM_ERR_DTYPE (-4)  /* unknown flag bits or w_dtype */
 #define GEMM_ERR_ALIAS (-5)  /* Y overlaps an input */
 #define GEMM_ERR_LAUNCH (-6) /* the HIP runtime reported an error at launch */
-#define GEMM_ERR_CONFIG (-7) /* a tile configuration index is out of range */
+#define GEMM_ERR_CONFIG (-7) /* a tile configuration index is out of range, or names a tile that keeps W in
+                                registers (suffix _wrN) with binary16 W */
 #define GEMM_ERR_WORKSPACE (-8) /* an explicit split-K configuration without a large enough workspace, or a
                                    workspace pointer and size that do not match (NULL with a nonzero size,
                                    or a negative size) */
@@ -138,7 +139,9 @@ int gemm_fwd_swiglu(const float *GATE, const float *UP, const void *W, const flo
  *                   without the stream's dispatch latency.  Nothing is
  *                   recorded when the status is negative or when there is
  *                   nothing to launch (an empty output).
- * An out-of-range config gives GEMM_ERR_CONFIG.
+ * An out-of-range config gives GEMM_ERR_CONFIG, and so does a forward
+ * configuration whose name ends in _wrN (W loaded straight into the compute
+ * waves' registers, fp32 only) with binary16 W.
  */
 typedef struct gemm_opts {
     int64_t config;

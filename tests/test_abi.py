@@ -87,17 +87,26 @@ def test_config_table(lib):
     def pick(M, K, N, sw, w16, ws=1):
         return lib.gemm_config_name(lib.gemm_select_config(M, K, N, sw, w16, ws)).decode()
     # the workload configurations (their tiles are the ones bench.py times)
-    assert pick(128, 768, 768, 0, 0) == "16x48x128_k4_sp4_dAW"
-    assert pick(512, 768, 768, 0, 0) == "32x48x128_k4_sp8_pf2_dAW"
-    assert pick(512, 3072, 768, 1, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
+    assert pick(128, 768, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(512, 768, 768, 0, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert pick(512, 3072, 768, 1, 0) == "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"
     assert pick(512, 768, 16384, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert pick(512, 768, 3072, 0, 1) == "128x48x32_w2x1_k2_sp4_pf3_il_dA"
     assert pick(8192, 3072, 768, 1, 1) == "64x384x32_w1x4_sp8_pf4_il"
     assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
-    # without a workspace the long-K small grid does not split K
-    assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"
-    assert pick(512, 3072, 768, 0, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"
-    assert pick(512, 3072, 768, 0, 0) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"
+    # small grids with fp32 W keep W in registers; f16 W stages it through LDS
+    assert pick(128, 768, 768, 0, 1) == "16x48x128_k4_sp4_dAW"
+    assert pick(512, 768, 768, 0, 1) == "32x48x128_k4_sp8_pf2_dAW"
+    assert pick(512, 1024, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(512, 1536, 768, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
+    # without a workspace the long-K small grid does not split K; with fp32 W
+    # a plain A does not split it either way
+    assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
+    assert pick(512, 3072, 768, 0, 0, ws=0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert pick(512, 3072, 768, 0, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert pick(512, 3072, 768, 1, 1) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"
+    assert pick(512, 3072, 768, 0, 1) == "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"
+    assert pick(512, 3072, 768, 1, 1, ws=0) == "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"
     # mid-size grids: 128 x 64 while it gives two tiles per CU, 64 x 64 when
     # it fills one whole round and 64 x 48 does not
     assert pick(512, 768, 8192, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
@@ -113,8 +122,11 @@ def test_workspace_sizes(lib):
     plus one M x N fp32 slot per split."""
     names = [lib.gemm_config_name(i).decode() for i in range(lib.gemm_num_configs())]
     CNT = 64 << 10
-    # 512 x 3072 x 768 SwiGLU: 32 x 96 tiles, K split in two
+    # 512 x 3072 x 768 SwiGLU: 16 x 192 tiles (fp32 W) or 32 x 96 (f16 W), K
+    # split in two
     assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 1, 0, -1) == CNT + 2 * 512 * 768 * 4
+    assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 1, 1, -1) == CNT + 2 * 512 * 768 * 4
+    assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 0, 0, -1) == 0
     assert lib.gemm_fwd_workspace_bytes(512, 768, 16384, 0, 1, -1) == 0
     assert lib.gemm_fwd_workspace_bytes(512, 3072, 768, 1, 0, names.index("128x128x32_w2x2_sp4_pf3_il_dA")) == 0
     ks8 = names.index("128x96x64_w2x2_sp8_ks8")
@@ -197,6 +209,16 @@ def test_dtype_and_config(lib):
     assert sw(lib, wd=-1) == _status("GEMM_ERR_DTYPE")
     assert fwd(lib, config=lib.gemm_num_configs()) == _status("GEMM_ERR_CONFIG")
     assert fwd(lib, config=-2) == _status("GEMM_ERR_CONFIG")
+    # tiles that keep W in registers are fp32-only: binary16 W is refused
+    # before anything is enqueued, also for an empty output
+    names = [lib.gemm_config_name(i).decode() for i in range(lib.gemm_num_configs())]
+    wr = [i for i, n in enumerate(names) if "_wr" in n]
+    assert len(wr) >= 4
+    for c in wr:
+        assert fwd(lib, flags=1, config=c) == _status("GEMM_ERR_CONFIG")
+        assert fwd(lib, flags=1, config=c, r=None) == _status("GEMM_ERR_CONFIG")
+        assert fwd(lib, flags=1, config=c, M=0) == _status("GEMM_ERR_CONFIG")
+        assert sw(lib, wd=1, config=c) == _status("GEMM_ERR_CONFIG")
 
 
 def test_workspace_validation(lib):

@@ -1,6 +1,8 @@
 """Parity in the configurations that the tile-choice rules for mid-size and
 batch-size grids pick (each test first checks that the rule picked it):
-the forward 128 x 64, 128 x 48 and 64 x 64 tiles, and the backward 128 x 64 (transposed
+the forward 128 x 64, 128 x 48 and 64 x 64 tiles, the forward 16 x 48 and
+16 x 96 tiles with W in registers (small grids, fp32 W; SwiGLU too), and the
+backward 128 x 64 (transposed
 B), 48 x 48 (long-contraction dW) and 96 x 96 (SwiGLU dW over a long
 contraction) tiles.  Large outputs are compared on sampled rows that include
 the last tile's rows."""
@@ -28,6 +30,11 @@ def _rows(M, seed, count=48, tail=128):
     (512, 768, 2048, True, False, "64x64x64_w2x2_sp4_dAW"),
     (512, 768, 3072, True, False, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
     (2048, 768, 772, False, True, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
+    # small grids with fp32 W: W in the compute waves' registers
+    (512, 1024, 1024, False, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (250, 768, 768, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (256, 768, 772, False, True, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
+    (512, 2000, 768, False, False, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
 ])
 def test_forward_rule(M, K, N, w16, resid, tile):
     from tiled_dense_gemm_matmul_amd import binding
@@ -37,6 +44,23 @@ def test_forward_rule(M, K, N, w16, resid, tile):
     y = run(c).cpu().numpy()
     rows = _rows(M, 7)
     check(c, y[rows], rows=rows, label=f"{M}x{K}x{N} {tile}")
+
+
+@pytest.mark.parametrize("M,K,N,ws,tile", [
+    (512, 1536, 768, True, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
+    (480, 2048, 800, True, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"),
+    (200, 2500, 772, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
+])
+def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.kernel_config(M, K, N, swiglu=True, workspace=ws) == tile
+    say(f"forward SwiGLU {M}x{K}x{N} workspace={ws} -> {tile}")
+    c = inputs.random_case(2000 + M + N, M, K, N, swiglu=True, residual=True, gate_scale=3.0)
+    y = binding.matmul_residual_swiglu_a(to_dev(c["G"]), to_dev(c["U"]), to_dev(c["W"]), to_dev(c["R"]),
+                                         use_workspace=ws)
+    torch.cuda.synchronize()
+    check(c, y.cpu().numpy(), label=f"{M}x{K}x{N} {tile}")
 
 
 def _cmp(y, ref, scale, label):

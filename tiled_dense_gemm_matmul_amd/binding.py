@@ -189,6 +189,13 @@ def config_name(config: int):
     return None if name is None else name.decode()
 
 
+def config_takes_w16(config: int) -> bool:
+    """Whether forward configuration `config` has binary16-W kernels: the
+    tiles that load W straight into the compute waves' registers (names
+    ending in _wrN) are fp32-only, and the library refuses them binary16 W."""
+    return "_wr" not in config_name(config)
+
+
 def bwd_num_configs() -> int:
     return load_library().gemm_bwd_num_configs()
 

@@ -60,6 +60,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
     const float *A;  // X, or GATE
@@ -251,7 +252,7 @@ __device__ __forceinline__ f16x4 load_f16x4(Rsrc r, int voff) {
 // work overlap on every SIMD (specialised pipeline).  PF: register sets of
 // staged K-stages per staging thread (1 to 5); loads run PF-1 stages ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_, int NP_, int PF_, int MINB_, int IL_ = 0,
-          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2, int DMA_ = 0>
+          int KS_ = 1, int CIL_ = 0, int PRIO_ = 2, int DMA_ = 0, int WR_ = 0>
 struct Tile {
     static constexpr bool CIL = CIL_ != 0;  // pipeline fragment reads one k-slice ahead of the MFMAs
     static constexpr int PRIO = PRIO_;      // wave priority of the staging waves
@@ -259,6 +260,12 @@ struct Tile {
     // (bit 0: plain fp32 A, bit 1: fp32 W) go from memory straight into the
     // LDS stage by buffer loads with the LDS destination, bypassing VGPRs.
     static constexpr int DMA = DMA_;
+    // Specialised pipeline, fp32 W in its natural layout only: WR > 0 keeps W
+    // out of LDS.  Each compute wave loads the W fragments of its own k-slices
+    // straight into a ring of WR slices of registers, WR - 1 slices ahead of
+    // its MFMAs; the LDS stages hold A alone.  (Other instantiations of such a
+    // tile stage W through LDS as usual.)
+    static constexpr int WR = WR_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WM = WM_, WN = WN_, WK = WK_;
     static constexpr int NP = NP_, PF = PF_, MINB = MINB_;
@@ -335,8 +342,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     constexpr int B_IT = (B_ITEMS + NS - 1) / NS;
     constexpr int ASTR = BM + 4;            // padded LDS row of a transposed A tile (floats)
     constexpr int BSTR = BN + 4;            // padded LDS row of the W tile (floats)
+    // W straight into the compute waves' registers (no W in LDS)
+    constexpr bool WREG = C::WR > 0 && SPEC && !W16 && !BT;
     constexpr int A_LDS = AT ? BK * ASTR : BM * BK;  // floats of the A tile
-    constexpr int B_LDS = BT ? BN * BK : BK * BSTR;
+    constexpr int B_LDS = WREG ? 0 : BT ? BN * BK : BK * BSTR;
     constexpr int STAGE = A_LDS + B_LDS;    // floats per LDS stage
     constexpr int CSTR = BN + 4;            // padded row of the output tile in LDS
     constexpr int CTILE = WK * BM * CSTR;   // floats for the output tile(s) in LDS
@@ -423,9 +432,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
 
     // Operands staged by LDS-destination loads, and the register items left.
     constexpr bool DMA_A = (C::DMA & 1) && !SWIGLU && SPEC && !AT;
-    constexpr bool DMA_W = (C::DMA & 2) && !W16 && SPEC && !BT;
+    constexpr bool DMA_W = (C::DMA & 2) && !W16 && SPEC && !BT && !WREG;
     constexpr int A_RIT = DMA_A ? 0 : A_IT;
-    constexpr int B_RIT = DMA_W ? 0 : B_IT;
+    constexpr int B_RIT = DMA_W || WREG ? 0 : B_IT;
     constexpr int REG_LOADS = A_RIT * (SWIGLU ? 2 : 1) + B_RIT;  // register loads per stage
     typedef StageRegs<A_RIT, B_RIT, SWIGLU, W16> Regs;
 
@@ -599,9 +608,119 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int r16 = lane & 15, q4 = lane >> 4;
-    auto compute_stage = [&](int buf) {
+
+    // W in registers (WREG).  For row 4*q4 + t of a 16-row k-slice, lane
+    // (q4, r16) holds TN columns of its wave tile: WG groups of WV
+    // consecutive columns, one load each, group g starting at column
+    // 16*WV*g + WV*r16 of the wave tile.  The wave's MFMA tile j takes
+    // column WV*r16 + j % WV of group j / WV, so the accumulators hold the
+    // wave tile's columns in a permuted order, undone where the epilogue
+    // parks them in LDS.  Groups never straddle N (N and WV*r16 are
+    // multiples of WV), so a group is either loaded whole or masked whole.
+    constexpr int WV = TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1;
+    constexpr int WG = TN / WV;
+    constexpr int NCH = CH / WK;            // k-slices per stage of one wave
+    constexpr int WR = WREG ? C::WR : 1;
+    static_assert(!WREG || (WR >= 2 && NCH % WR == 0), "W ring slots must divide a stage's slices");
+    int wr_off[WREG ? 4 : 1][WREG ? WG : 1];
+    float wring[WR][WREG ? 4 : 1][WREG ? TN : 1];
+    if constexpr (WREG) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g = 0; g < WG; ++g) {
+                const int col = wn * WTN + g * 16 * WV + WV * r16;
+                wr_off[t][g] = n0 + col < N ? ((4 * q4 + t) * N + col) * 4 : kOOB;
+            }
+    }
+    // The W fragments of the 16-row slice starting at row kk, from a resource
+    // that holds the slice's rows inside the K range (none past it).
+    // W's tile origin as a wave-uniform 64-bit value, so that the per-slice
+    // resource base is scalar arithmetic (readfirstlane returns a signed
+    // int: each half goes through uint32_t before it is widened)
+    const uint32_t wtile_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uint64_t>(Wbase)));
+    const uint32_t wtile_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uint64_t>(Wbase) >> 32));
+    const uint64_t wtile = (static_cast<uint64_t>(wtile_hi) << 32) | wtile_lo;
+    auto wload = [&](float (&d)[WREG ? 4 : 1][WREG ? TN : 1], int kk) {
+        if constexpr (WREG) {
+            const int rem = kend - kk;
+            const Rsrc rW = make_rsrc(reinterpret_cast<const void *>(wtile + (uint64_t)(uint32_t)kk * (uint32_t)(N * 4)),
+                                      rem > 0 ? min(rem, 16) * N * 4 : 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int g = 0; g < WG; ++g) {
+                    if constexpr (WV == 4) {
+                        const f32x4 v = load_f32x4(rW, wr_off[t][g]);
+#pragma unroll
+                        for (int v4 = 0; v4 < 4; ++v4) d[t][g * 4 + v4] = v[v4];
+                    } else if constexpr (WV == 2) {
+                        const f32x2 v = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rW, wr_off[t][g], 0, 0));
+                        d[t][g * 2] = v[0];
+                        d[t][g * 2 + 1] = v[1];
+                    } else {
+                        d[t][g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rW, wr_off[t][g], 0, 0));
+                    }
+                }
+        }
+    };
+
+    auto compute_stage = [&](int buf, int k0) {
         const float *As = lds + buf * STAGE;
         const float *Bs = As + A_LDS;
+        if constexpr (WREG) {
+            (void)Bs;
+            // The A fragments of slice l + 1 are read while slice l is
+            // multiplied; the W loads of slice l + WR - 1 go out between the
+            // MFMAs of slice l.  Each slice is its own scheduling region, so
+            // the compiler can neither sink those loads to their use nor
+            // hoist the next slice's reads above them.
+            auto read_a = [&](f32x4 (&af)[TM], int c) {
+                const int slot = c * 4 + q4;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    if constexpr (AT) {
+                        const float *a = As + (c * 16 + q4 * 4) * ASTR + wm * WTM + i * 16 + r16;
+                        af[i] = f32x4{a[0], a[ASTR], a[2 * ASTR], a[3 * ASTR]};
+                    } else {
+                        const int row = wm * WTM + i * 16 + r16;
+                        af[i] = *reinterpret_cast<const f32x4 *>(As + (row * SL + (slot ^ swz<SL>(row))) * 4);
+                    }
+                }
+            };
+            constexpr int DS = AT ? 2 * TM : TM;  // LDS reads per slice
+            constexpr int NL = 4 * WG;             // W loads per slice
+            constexpr int MF = 4 * TM * TN;        // MFMAs per slice
+            constexpr int PER = MF / NL > 0 ? MF / NL : 1;
+            f32x4 afc[TM], afn[TM];
+            read_a(afc, wk);
+#pragma unroll
+            for (int l = 0; l < NCH; ++l) {
+                if (l + 1 < NCH) read_a(afn, wk + (l + 1) * WK);
+                // slice l + WR - 1 (of this stage or the next) into the ring
+                // slot that slice l - 1 used
+                const int la = l + WR - 1;
+                wload(wring[la % WR], k0 + (la < NCH ? (wk + la * WK) * 16 : BK + (wk + (la - NCH) * WK) * 16));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(afc[i][t], wring[l % WR][t][j], acc[i][j], 0, 0, 0);
+                if (l + 1 < NCH) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+#pragma unroll
+                for (int x = 0; x < NL; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+                }
+                if constexpr (MF > NL * PER) __builtin_amdgcn_sched_group_barrier(0x008, MF - NL * PER, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) afc[i] = afn[i];
+            }
+            return;
+        }
 #pragma unroll
         for (int c = wk; c < CH; c += WK) {
             const int slot = c * 4 + q4;
@@ -636,12 +755,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][t], bf[j][t], acc[i][j], 0, 0, 0);
         }
-        if constexpr (C::CIL) {
+        if constexpr (C::CIL && !WREG) {
             // Scheduling hint: read all fragments of the first k-slice, then
             // spread each later slice's reads over the MFMAs of the slice
             // before it, so LDS latency hides behind matrix work instead of
             // stalling in front of every few MFMAs.
-            constexpr int NCH = CH / WK;
             // b128 per contraction-contiguous fragment, two read2_b32 per other
             constexpr int DS = (AT ? 2 * TM : TM) + (BT ? TN : 2 * TN);
             constexpr int MF = 4 * TM * TN;
@@ -668,8 +786,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
     // while the VALU works instead of stalling the wave at issue.
     auto interleave_hint = [&]() {
         if constexpr (C::IL) {
-            constexpr int NLOAD = A_IT * (SWIGLU ? 2 : 1) + B_IT;
-            constexpr int NVALU = (SWIGLU ? 24 * A_IT : 0) + (W16 ? 4 * B_IT : 0) + 2 * (A_IT + B_IT);
+            constexpr int NLOAD = A_IT * (SWIGLU ? 2 : 1) + (WREG ? 0 : B_IT);
+            constexpr int NVALU = (SWIGLU ? 24 * A_IT : 0) + (W16 ? 4 * B_IT : 0) + 2 * (A_IT + (WREG ? 0 : B_IT));
             constexpr int PER = (NVALU + NLOAD - 1) / NLOAD;
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
@@ -778,12 +896,19 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             return;
         }
         if (nstages > 0) {
+            if constexpr (WREG) {
+#pragma unroll
+                for (int l = 0; l + 1 < WR; ++l) wload(wring[l], kbeg + (wk + l * WK) * 16);
+            }
             stage_barrier();
             for (int s = 0;; ++s) {
-                compute_stage(s & 1);
+                compute_stage(s & 1, kbeg + s * BK);
                 stage_barrier();
                 if (s + 1 >= nstages) break;
             }
+            // the ring's last loads (past the K range, so zeros) land before
+            // their registers are reused
+            if constexpr (WREG) wait_vmcnt<0>();
         }
     } else if (nstages > 0) {
         if constexpr (C::PF == 2) {
@@ -794,12 +919,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             stage_barrier();
             for (int s = 0;; s += 2) {
                 load_stage(r0, kbeg + (s + 2) * BK);
-                compute_stage(0);
+                compute_stage(0, 0);
                 store_stage(r1, 1);
                 stage_barrier();
                 if (s + 1 >= nstages) break;
                 load_stage(r1, kbeg + (s + 3) * BK);
-                compute_stage(1);
+                compute_stage(1, 0);
                 store_stage(r0, 0);
                 stage_barrier();
                 if (s + 2 >= nstages) break;
@@ -811,7 +936,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             stage_barrier();
             for (int s = 0;; ++s) {
                 load_stage(r0, kbeg + (s + 1) * BK);
-                compute_stage(s & 1);
+                compute_stage(s & 1, 0);
                 if (s + 1 >= nstages) break;
                 store_stage(r0, (s + 1) & 1);
                 stage_barrier();
@@ -836,7 +961,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_fwd_kernel(Params p) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Ct[(wm * WTM + i * 16 + q4 * 4 + r) * CSTR + wn * WTN + j * 16 + r16] = acc[i][j][r];
+                    Ct[(wm * WTM + i * 16 + q4 * 4 + r) * CSTR + wn * WTN +
+                       (WREG ? (j / WV) * 16 * WV + WV * r16 + j % WV : j * 16 + r16)] = acc[i][j][r];
     }
     stage_barrier();
 
@@ -968,16 +1094,24 @@ struct ConfigEntry {
     KernelFn fn[2][2][2];  // [swiglu][w16][resid]
 };
 
+// A tile that keeps W in registers (WR > 0) exists for fp32 W only: its
+// f16 W slots are empty and such a call gives GEMM_ERR_CONFIG.
+template <class C, bool SWIGLU, bool W16, bool RESID>
+constexpr KernelFn fwd_fn() {
+    if constexpr (W16 && C::WR > 0) return nullptr;
+    else return gemm_fwd_kernel<C, SWIGLU, W16, RESID>;
+}
+
 template <class C>
 constexpr ConfigEntry make_entry(const char *name) {
     return ConfigEntry{name, C::BM, C::BN, C::BK, C::NT, C::KS,
-                       {{{gemm_fwd_kernel<C, false, false, false>, gemm_fwd_kernel<C, false, false, true>},
-                         {gemm_fwd_kernel<C, false, true, false>, gemm_fwd_kernel<C, false, true, true>}},
-                        {{gemm_fwd_kernel<C, true, false, false>, gemm_fwd_kernel<C, true, false, true>},
-                         {gemm_fwd_kernel<C, true, true, false>, gemm_fwd_kernel<C, true, true, true>}}}};
+                       {{{fwd_fn<C, false, false, false>(), fwd_fn<C, false, false, true>()},
+                         {fwd_fn<C, false, true, false>(), fwd_fn<C, false, true, true>()}},
+                        {{fwd_fn<C, true, false, false>(), fwd_fn<C, true, false, true>()},
+                         {fwd_fn<C, true, true, false>(), fwd_fn<C, true, true, true>()}}}};
 }
 
-// Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL, PRIO, DMA>: the
+// Tile<BM, BN, BK, WM, WN, WK, NP, PF, MINB, IL, KS, CIL, PRIO, DMA, WR>: the
 // tiles the library's own forward choice takes (select_config), then one of
 // each other kind of pipeline, so that every code path stays built and
 // tested.
@@ -994,6 +1128,11 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 3>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    // W in the compute waves' registers (fp32 W only)
+    make_entry<Tile<16, 192, 128, 1, 4, 1, 4, 3, 1, 1, 2, 0, 2, 0, 4>>("16x192x128_w1x4_sp4_pf3_il_ks2_wr4"),
+    make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 2, 1, 1, 1, 0, 2, 0, 4>>("16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
+    make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_dA_wr2"),
     // specialised, register staging only, two stages of loads in flight
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
     // specialised, three stages in flight without the interleaving hint,
@@ -1104,24 +1243,34 @@ bool same_name(const char *a, const char *b) {
 // 512 x 768 x 3072 with f16 W, 32.9 against 36.2 at 1024 x 768 x 1536 and
 // 40.6 against 44.3 at 2048 x 1024 x 768 with SwiGLU, level (within 0.5%)
 // at 2048 x 768 x 768 and 512 x 1024 x 3072.
-// The smallest forward grids stage 128-deep slices of K two at a time with
-// eight staging waves: at 512 x 768 x 768, one 32 x 48 tile per CU, 7.6
-// against 9.3 us with 64-deep slices three at a time and four staging waves
-// (8.1 against 9.7 with R), timed between the other products of the seq-512
-// layer; 16.1 against 17.5 us at 512 x 1536 x 768 with SwiGLU and 12.5
-// against 16.1 without (one shape measured the other way: 512 x 1024 x 1024
-// with f16 W, 18.7 against 17.2 us).
-// Long K on a small grid splits K over two workgroups when the caller
-// provides a workspace (`split`), with 128-deep slices of K and, for a plain
-// A, LDS-destination loads of A too (512 x 3072 x 768: 26.0 us with SwiGLU;
-// 23.4 against 25.3 us with 64-deep slices for a plain A).  Without a
-// workspace, 16 x 96 tiles over the whole K, with 128-deep slices split over
-// two waves and W by LDS-destination loads: 26.6 against 39.2 us for 64-deep
-// slices split over four waves with SwiGLU, 25.7 against 34.7 for a plain A.
+// With f16 W (and in the backward rule), the smallest grids stage 128-deep
+// slices of K two at a time with eight staging waves (measured with fp32 W
+// before the tiles below existed: at 512 x 768 x 768, one 32 x 48 tile per
+// CU, 7.6 against 9.3 us with 64-deep slices three at a time and four
+// staging waves; 16.1 against 17.5 us at 512 x 1536 x 768 with SwiGLU; one
+// shape measured the other way: 512 x 1024 x 1024 with f16 W, 18.7 against
+// 17.2 us), and a long K splits over two workgroups when the caller provides
+// a workspace (`split`), with 128-deep slices, or without one takes 16 x 96
+// tiles over the whole K (measured with fp32 W: 26.6 against 39.2 us for
+// 64-deep slices split over four waves at 512 x 3072 x 768 with SwiGLU).
+// Small grids with fp32 W (forward products only) take tiles of 16 rows
+// that keep W in the compute waves' registers, so that the LDS holds A
+// alone; W16 tiles of that kind do not exist.  With SwiGLU and a long K and
+// a workspace: 16 x 192 tiles with K split in two, which combine each
+// element of A four times instead of eight (512 x 3072 x 768: 24.0 against
+// 26.0 us for 32 x 96 tiles with W staged through LDS).  Otherwise 16 x 96
+// tiles (SwiGLU: eight staging waves; 24.9 against 26.6 us at
+// 512 x 3072 x 768 without a workspace, 14.1 against 16.2 at 512 x 1536 x 768)
+// or, for a plain A, 16 x 48 tiles where those fill the CUs in better
+// proportion (whole rounds of 256 workgroups): 512 x 1024 x 1024 in 12.7
+// against 14.6 us for 16 x 96 and 16.6 for 32 x 48 with W in LDS,
+// 128 x 768 x 768 in 4.5 against 5.8, 512 x 3072 x 768 in 20.8 (16 x 96)
+// against 21.9, whether or not there is a workspace.
 // `forward` false: the rule as the backward products measured it, without
-// the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice and the
-// 128-deep slices; every name it gives is in the backward table.
-const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split, bool forward) {
+// the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice, the
+// 128-deep slices and W in registers; every name it gives is in the
+// backward table.
+const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward) {
     const int64_t cus = 256;
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
     if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return "64x384x32_w1x4_sp8_pf4_il";
@@ -1136,6 +1285,18 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split,
     // (and widens, or combines) each block of W (or A) half as often
     if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
     if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
+    if (forward && !w16) {
+        if (swiglu) {
+            if (K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
+                return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
+            return "16x96x128_w1x2_k2_sp8_pf2_il_wr4";
+        }
+        // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
+        auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
+        return fill(ceil_div(M, 16) * ceil_div(N, 96)) >= fill(ceil_div(M, 16) * ceil_div(N, 48))
+                   ? "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+                   : "16x48x128_k4_sp4_pf3_il_dA_wr2";
+    }
     if (M <= 128) return "16x48x128_k4_sp4_dAW";
     if (K >= 2048) {
         // long K on a small grid: split K in two when there is a workspace
@@ -1152,8 +1313,7 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, bool split,
 // The forward choice: an index into kConfigs (-1 if the rule names a tile
 // the table lacks, which would be a build error in spirit).
 int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split) {
-    (void)w16;
-    return config_index(select_rule(M, K, N, swiglu, split, true));
+    return config_index(select_rule(M, K, N, swiglu, w16, split, true));
 }
 
 // Tile choice for the backward products, by their kernel dimensions (output
@@ -1190,7 +1350,7 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     const int64_t cus = 256;
     // the shared rule without its SwiGLU and forward-only tiles, which the
     // backward table does not hold
-    const char *f = select_rule(M, K, N, 0, split, false);
+    const char *f = select_rule(M, K, N, 0, 0, split, false);
     if (op == kOpNT && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus && ceil_div(M, 128) * ceil_div(N, 128) < 2 * cus)
         return bwd("128x64x32_w2x2_sp4_pf3_il_dA");
     // without split-K the rule's long-K choice is the deep tile
@@ -1305,6 +1465,9 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     if (overlaps(o.ws, wsb, Y, ybytes) || overlaps(o.ws, wsb, A, abytes) || overlaps(o.ws, wsb, U, abytes) ||
         overlaps(o.ws, wsb, W, wbytes) || overlaps(o.ws, wsb, R, ybytes))
         return GEMM_ERR_ALIAS;
+    // an explicit tile that keeps W in registers exists for fp32 W only
+    if (o.config >= 0 && kConfigs[o.config].fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0] == nullptr)
+        return GEMM_ERR_CONFIG;
     if (M == 0 || N == 0) return GEMM_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1337,6 +1500,7 @@ int run(bool swiglu, const float *A, const float *U, const void *W, bool w16, co
     const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * e.ks;
     if (blocks >= lim) return GEMM_ERR_SHAPE;
     KernelFn fn = e.fn[swiglu ? 1 : 0][w16 ? 1 : 0][R ? 1 : 0];
+    if (!fn) return GEMM_ERR_CONFIG;
     // with NULL events this is a plain launch; otherwise the events take the
     // kernel's own start and end times
     hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(e.nt), 0, s, static_cast<hipEvent_t>(o.start),
@@ -1654,7 +1818,7 @@ const char *gemm_status_string(int status) {
         case GEMM_ERR_DTYPE: return "unknown flags or weight type";
         case GEMM_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
-        case GEMM_ERR_CONFIG: return "tile configuration index out of range";
+        case GEMM_ERR_CONFIG: return "tile configuration index out of range, or a W-in-registers tile with binary16 W";
         case GEMM_ERR_WORKSPACE: return "the workspace is missing or smaller than the configuration needs";
         default: return "unknown status";
     }
