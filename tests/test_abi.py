@@ -320,8 +320,10 @@ def test_backward_selection(lib):
     # dW of the 768 x 768 projections: 384 tiles of 32 x 48 would take two
     # rounds on 256 CUs, 256 tiles of 48 x 48 take one
     assert name(2, 512, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
-    assert name(2, 512, 768, 3072) == "32x48x64_k4_sp4_pf3_dAW"
-    assert name(2, 512, 3072, 768) == "32x48x64_k4_sp4_pf3_dAW"
+    # dW over the 512-token contraction whose 32 x 96 grid fills the CUs: dY
+    # straight into registers
+    assert name(2, 512, 768, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert name(2, 512, 3072, 768) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(1, 512, 768, 16384) == "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"
     assert name(1, 512, 3072, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(1, 512, 768, 3072) == "16x48x128_k4_sp4_dAW"
@@ -336,7 +338,7 @@ def test_backward_selection(lib):
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1, 1)).decode() == \
         "96x96x64_w2x2_sp4_pf3_il_dA"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1, 1)).decode() == \
-        "32x48x64_k4_sp4_pf3_dAW"
+        "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
 
 
 def test_loss_exports_and_validation(lib):
