@@ -99,6 +99,8 @@ def test_config_table(lib):
     assert pick(512, 768, 768, 0, 1) == "32x48x128_k4_sp8_pf2_dAW"
     assert pick(512, 1024, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     assert pick(512, 1536, 768, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
+    assert pick(128, 3072, 768, 1, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(256, 768, 1024, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
     # without a workspace the long-K small grid does not split K; with fp32 W
     # a plain A does not split it either way
     assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"

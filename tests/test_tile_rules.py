@@ -49,7 +49,8 @@ def test_forward_rule(M, K, N, w16, resid, tile):
 @pytest.mark.parametrize("M,K,N,ws,tile", [
     (512, 1536, 768, True, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
     (480, 2048, 800, True, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"),
-    (200, 2500, 772, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
+    (200, 2500, 772, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (384, 2048, 768, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
 ])
 def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):
     import torch

@@ -1264,11 +1264,13 @@ bool same_name(const char *a, const char *b) {
 // 26.0 us for 32 x 96 tiles with W staged through LDS).  Otherwise 16 x 96
 // tiles (SwiGLU: eight staging waves; 24.9 against 26.6 us at
 // 512 x 3072 x 768 without a workspace, 14.1 against 16.2 at 512 x 1536 x 768)
-// or, for a plain A, 16 x 48 tiles where those fill the CUs in better
-// proportion (whole rounds of 256 workgroups): 512 x 1024 x 1024 in 12.7
-// against 14.6 us for 16 x 96 and 16.6 for 32 x 48 with W in LDS,
-// 128 x 768 x 768 in 4.5 against 5.8, 512 x 3072 x 768 in 20.8 (16 x 96)
-// against 21.9, whether or not there is a workspace.
+// or 16 x 48 tiles where those fill the CUs in better proportion (whole
+// rounds of 256 workgroups): 512 x 1024 x 1024 in 12.7 against 14.6 us for
+// 16 x 96 and 16.6 for 32 x 48 with W in LDS, 128 x 768 x 768 in 4.5 against
+// 5.8; with SwiGLU 128 x 3072 x 768 in 17.2 against 24.3 for 16 x 96 and 21.5
+// for 16 x 48 with W in LDS, 256 x 1536 x 768 in 10.0 against 14.0.  A plain
+// A is never split over workgroups (512 x 3072 x 768: 20.8 us for 16 x 96
+// against 21.9 for the fastest split).
 // `forward` false: the rule as the backward products measured it, without
 // the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice, the
 // 128-deep slices and W in registers; every name it gives is in the
@@ -1289,16 +1291,13 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
     if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
     if (forward && !w16) {
-        if (swiglu) {
-            if (K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
-                return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
-            return "16x96x128_w1x2_k2_sp8_pf2_il_wr4";
-        }
+        if (swiglu && K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
+            return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
         // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
         auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
-        return fill(ceil_div(M, 16) * ceil_div(N, 96)) >= fill(ceil_div(M, 16) * ceil_div(N, 48))
-                   ? "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
-                   : "16x48x128_k4_sp4_pf3_il_dA_wr2";
+        if (fill(ceil_div(M, 16) * ceil_div(N, 96)) < fill(ceil_div(M, 16) * ceil_div(N, 48)))
+            return "16x48x128_k4_sp4_pf3_il_dA_wr2";
+        return swiglu ? "16x96x128_w1x2_k2_sp8_pf2_il_wr4" : "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
     }
     if (M <= 128) return "16x48x128_k4_sp4_dAW";
     if (K >= 2048) {
