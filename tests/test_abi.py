@@ -101,6 +101,11 @@ def test_config_table(lib):
     assert pick(512, 1536, 768, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
     assert pick(128, 3072, 768, 1, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     assert pick(256, 768, 1024, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
+    # mid-size fp32 grids: 32 x 192 on whole rounds, else 16 x 96 / 16 x 48
+    assert pick(2048, 768, 768, 0, 0) == "32x192x64_w1x4_sp4_pf3_il_dA_wr4"
+    assert pick(2048, 768, 768, 0, 1) == "128x48x32_w2x1_k2_sp4_pf3_il_dA"
+    assert pick(768, 768, 2048, 1, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert pick(1000, 768, 772, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     # without a workspace the long-K small grid does not split K; with fp32 W
     # a plain A does not split it either way
     assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"

@@ -29,11 +29,14 @@ def _rows(M, seed, count=48, tail=128):
     (8192, 768, 768, False, True, "128x64x32_w2x2_sp4_pf3_il_dA"),
     (512, 768, 2048, True, False, "64x64x64_w2x2_sp4_dAW"),
     (512, 768, 3072, True, False, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
-    (2048, 768, 772, False, True, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
+    (2048, 768, 772, True, True, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
     # small grids with fp32 W: W in the compute waves' registers
     (512, 1024, 1024, False, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (250, 768, 768, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (256, 768, 772, False, True, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
+    (2048, 768, 772, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (2048, 768, 768, False, False, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
+    (2040, 768, 760, False, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (512, 2000, 768, False, False, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
 ])
 def test_forward_rule(M, K, N, w16, resid, tile):
@@ -50,6 +53,8 @@ def test_forward_rule(M, K, N, w16, resid, tile):
     (512, 1536, 768, True, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
     (480, 2048, 800, True, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"),
     (200, 2500, 772, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (768, 768, 2048, True, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
+    (1000, 768, 1532, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (384, 2048, 768, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
 ])
 def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):

@@ -1133,6 +1133,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 2, 1, 1, 1, 0, 2, 0, 4>>("16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
     make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    make_entry<Tile<32, 192, 64, 1, 4, 1, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     // specialised, register staging only, two stages of loads in flight
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
     // specialised, three stages in flight without the interleaving hint,
@@ -1256,21 +1257,26 @@ bool same_name(const char *a, const char *b) {
 // a workspace (`split`), with 128-deep slices, or without one takes 16 x 96
 // tiles over the whole K (measured with fp32 W: 26.6 against 39.2 us for
 // 64-deep slices split over four waves at 512 x 3072 x 768 with SwiGLU).
-// Small grids with fp32 W (forward products only) take tiles of 16 rows
-// that keep W in the compute waves' registers, so that the LDS holds A
-// alone; W16 tiles of that kind do not exist.  With SwiGLU and a long K and
-// a workspace: 16 x 192 tiles with K split in two, which combine each
-// element of A four times instead of eight (512 x 3072 x 768: 24.0 against
-// 26.0 us for 32 x 96 tiles with W staged through LDS).  Otherwise 16 x 96
-// tiles (SwiGLU: eight staging waves; 24.9 against 26.6 us at
-// 512 x 3072 x 768 without a workspace, 14.1 against 16.2 at 512 x 1536 x 768)
-// or 16 x 48 tiles where those fill the CUs in better proportion (whole
-// rounds of 256 workgroups): 512 x 1024 x 1024 in 12.7 against 14.6 us for
-// 16 x 96 and 16.6 for 32 x 48 with W in LDS, 128 x 768 x 768 in 4.5 against
-// 5.8; with SwiGLU 128 x 3072 x 768 in 17.2 against 24.3 for 16 x 96 and 21.5
-// for 16 x 48 with W in LDS, 256 x 1536 x 768 in 10.0 against 14.0.  A plain
-// A is never split over workgroups (512 x 3072 x 768: 20.8 us for 16 x 96
-// against 21.9 for the fastest split).
+// Grids below those of the larger tiles, with fp32 W (forward products
+// only), take tiles that keep W in the compute waves' registers, so that the
+// LDS holds A alone; W16 tiles of that kind do not exist.  32 x 192 tiles
+// where their grid fills whole rounds of the 256 CUs (2048 x 768 x 768: 20.9
+// against 21.8 us for 128 x 48; 1024 x 768 x 1536 with SwiGLU: 23.7 against
+// 32.2).  With SwiGLU and a long K and a workspace: 16 x 192 tiles with K
+// split in two, which combine each element of A four times instead of eight
+// (512 x 3072 x 768: 24.0 against 26.0 us for 32 x 96 tiles with W staged
+// through LDS).  Otherwise 16 x 96 tiles, or 16 x 48 where their grid fills
+// whole rounds better (for SwiGLU, which they combine twice as often, only
+// when the 16 x 96 grid is below one round): 512 x 1024 x 1024 in 12.7
+// against 14.6 us for 16 x 96 and 16.6 for 32 x 48 with W in LDS,
+// 128 x 768 x 768 in 4.5 against 5.8, 1000 x 768 x 772 in 14.9 against 17.3;
+// with SwiGLU 128 x 3072 x 768 in 17.2 against 24.3, but 768 x 768 x 2048 in
+// 32.0 on 16 x 96 against 33.2 (and 59.8 for 128 x 48).  With SwiGLU the
+// 16 x 96 tiles use eight staging waves up to one round (24.9 against 26.6 us
+// at 512 x 3072 x 768 without a workspace) and four beyond, where two
+// workgroups then share a CU (2000 x 1000 x 780: 40.6 against 44.8).  A
+// plain A is never split over workgroups (512 x 3072 x 768: 20.8 us for
+// 16 x 96 against 21.9 for the fastest split).
 // `forward` false: the rule as the backward products measured it, without
 // the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice, the
 // 128-deep slices and W in registers; every name it gives is in the
@@ -1286,19 +1292,28 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
     if (t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
     if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return "64x64x64_w2x2_sp4_dAW";
+    // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
+    auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
+    if (forward && !w16) {
+        // every smaller grid with fp32 W: tiles with W in registers; 32 x 192
+        // where that grid fills whole rounds of the CUs (nine tenths or more)
+        const int64_t t32w = ceil_div(M, 32) * ceil_div(N, 192);
+        if (t32w >= cus && fill(t32w) >= 0.9) return "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
+        if (swiglu && K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
+            return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
+        // 16 x 48 where its grid fills whole rounds better (with SwiGLU,
+        // which it combines twice as often, only below one round of 16 x 96)
+        const int64_t s96 = ceil_div(M, 16) * ceil_div(N, 96), s48 = ceil_div(M, 16) * ceil_div(N, 48);
+        if (fill(s96) < fill(s48) && (!swiglu || s96 < cus)) return "16x48x128_k4_sp4_pf3_il_dA_wr2";
+        // SwiGLU on one round at most: eight staging waves; otherwise four,
+        // which lets two workgroups share a CU
+        if (swiglu && s96 <= cus) return "16x96x128_w1x2_k2_sp8_pf2_il_wr4";
+        return "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
+    }
     // forward products: 128 x 48 where that grid fills the CUs, which stages
     // (and widens, or combines) each block of W (or A) half as often
     if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
     if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
-    if (forward && !w16) {
-        if (swiglu && K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
-            return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
-        // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
-        auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
-        if (fill(ceil_div(M, 16) * ceil_div(N, 96)) < fill(ceil_div(M, 16) * ceil_div(N, 48)))
-            return "16x48x128_k4_sp4_pf3_il_dA_wr2";
-        return swiglu ? "16x96x128_w1x2_k2_sp8_pf2_il_wr4" : "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
-    }
     if (M <= 128) return "16x48x128_k4_sp4_dAW";
     if (K >= 2048) {
         // long K on a small grid: split K in two when there is a workspace
