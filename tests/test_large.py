@@ -1,9 +1,11 @@
 """Operands past 4 GiB.
 
 The ABI accepts M up to 2^31 - 1.  The kernels keep 32-bit offsets only
-inside a tile (at most 256 rows of A or Y) or a K-stage, and address each
-tile and each stage from a 64-bit base, so an array larger than 2^32 bytes
-must come out right in its last tiles as in its first.  Here A (and UP) hold
+inside a tile (at most 256 rows of A or Y), a K-stage or a 16-row slice of
+W, and address each tile, stage and slice from a 64-bit base, so an array
+larger than 2^32 bytes must come out right in its last tiles as in its
+first: with the library's choice and with a tile that loads W into
+registers.  Here A (and UP) hold
 2^20 + 37 rows of 1024 fp32 values, 4.3e9 bytes each; the weight gradient
 contracts over those 2^20 + 37 rows.  Inputs are drawn on the device from
 seeded generators (N(0, 1), weights scaled by 0.02).  The forward products
@@ -35,17 +37,19 @@ def _rows(M):
                                      np.arange(M - 300, M)])).astype(np.int64)
 
 
+@pytest.mark.parametrize("tile", [None, "16x48x128_k4_sp4_pf3_il_dA_wr2"])
 @pytest.mark.parametrize("swiglu", [False, True])
-def test_forward_operands_past_4gib(swiglu):
+def test_forward_operands_past_4gib(swiglu, tile):
     import torch
     from tiled_dense_gemm_matmul_amd import binding
-    say(f"forward swiglu={swiglu}: A {M_BIG}x{K} fp32 ({M_BIG * K * 4 / 2**30:.2f} GiB), N={N}, "
-        f"tile {binding.kernel_config(M_BIG, K, N, swiglu=swiglu)}")
+    cfg = None if tile is None else next(i for i in range(binding.num_configs()) if binding.config_name(i) == tile)
+    name = binding.kernel_config(M_BIG, K, N, swiglu=swiglu) if tile is None else tile
+    say(f"forward swiglu={swiglu}: A {M_BIG}x{K} fp32 ({M_BIG * K * 4 / 2**30:.2f} GiB), N={N}, tile {name}")
     A = _randn((M_BIG, K), 11)
     U = _randn((M_BIG, K), 12) if swiglu else None
     W = _randn((K, N), 13, 0.02)
     R = _randn((M_BIG, N), 14)
-    y = binding.matmul_residual_swiglu_a(A, U, W, R) if swiglu else binding.matmul(A, W, R)
+    y = binding.matmul_residual_swiglu_a(A, U, W, R, config=cfg) if swiglu else binding.matmul(A, W, R, config=cfg)
     torch.cuda.synchronize()
     rows = _rows(M_BIG)
     idx = torch.from_numpy(rows).to(device())
