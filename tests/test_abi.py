@@ -340,10 +340,13 @@ def test_backward_selection(lib):
     assert name(1, 8192, 768, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 8192, 3072, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
-    assert name(2, 8192, 768, 3072) == "48x48x64_k4_sp4_pf3_dAW"
-    assert name(2, 8192, 1024, 4096) == "32x48x64_k4_sp4_pf3_dAW"
+    # dW whose 32 x 96 grid fills whole rounds: dY into registers, whatever
+    # the contraction
+    assert name(2, 8192, 768, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert name(2, 8192, 1024, 4096) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert name(2, 2048, 1024, 1024) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1, 1)).decode() == \
-        "96x96x64_w2x2_sp4_pf3_il_dA"
+        "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1, 1)).decode() == \
         "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
 

@@ -1179,9 +1179,6 @@ const ConfigEntry kBwdConfigs[] = {
     // a transposed B whose grid of 128 x 64 tiles comes to two per CU
     // (the 8192-token dX of the attention projections and of gate/up)
     make_bwd_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
-    // the SwiGLU weight gradient over a long contraction: G and U re-staged
-    // once per 96 output columns instead of once per 48
-    make_bwd_entry<Tile<96, 96, 64, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("96x96x64_w2x2_sp4_pf3_il_dA"),
     // weight gradients over a short contraction: dY (B in its natural
     // layout) straight into the compute waves' registers
     make_bwd_entry<Tile<32, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
@@ -1336,32 +1333,32 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // Tile choice for the backward products, by their kernel dimensions (output
 // rows, contraction, output columns): the shared rule (select_rule with
 // `forward` false), with these exceptions measured on the seq-512 model's
-// backward shapes.  A transposed A is read
-// with four LDS reads per fragment, so with a short contraction the 64 x 64
+// backward shapes and their 8192-token batch.  A transposed A is read with
+// four LDS reads per fragment, so with a short contraction the 64 x 64
 // tiles lose to 32 x 48 tiles with the K range split over four waves (about
 // 20% at 768 x 512 x 3072 and 3072 x 512 x 768).  With a transposed B and a
 // contraction of a few thousand, 16 x 48 tiles with BK = 128 beat the
 // two-workgroup split-K (6% at 512 x 3072 x 768).  With a contraction of
 // 8192 or more, 128 x 96 tiles with the K range split eight ways re-read the
 // transposed B a quarter as often as 32 x 96 tiles and win by 12% (the
-// lm_head's dX, 512 x 16384 x 768).  And where those 32 x 48 tiles of a
+// lm_head's dX, 512 x 16384 x 768).  Where those 32 x 48 tiles of a
 // transposed A come to between one and two per CU while 48 x 48 tiles come
 // to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
 // at 768 x 512 x 768, and 98 against over 125 us for the 16 x 96 tiles the
-// forward rule picks at 768 x 8192 x 768.  A transposed B takes 128 x 64
-// tiles where they come to two per CU and 128 x 128 tiles do not: 74 against
-// 80 us at 8192 x 768 x 768 and 282 against over 300 at 8192 x 3072 x 768.
-// The SwiGLU weight gradient over a contraction of 4096 or more takes
-// 96 x 96 tiles where they fill the CUs, combining G and U half as often:
-// 346 against 364 us at 3072 x 8192 x 768.  Other weight gradients over a
-// contraction of 4096 or more take 48 x 48 tiles too where the output splits
-// into whole ones: 311 against 331 us at 3072 x 8192 x 768, 610 against 638
-// at 768 x 16384 x 3072 (with ragged 48-row tiles, 1024 x 8192 x 4096, they
-// lose 3%).  Weight gradients over a shorter contraction whose 32 x 96 grid
-// fills the CUs take 32 x 96 tiles that load dY straight into the compute
-// waves' registers (LDS then holds the transposed A alone): 23.2 against
-// 24.9 us at 768 x 512 x 3072 (24.1 against 25.7 accumulating), 26.4
-// against 27.7 at 3072 x 512 x 768 with SwiGLU.  The split-K tiles need the caller's workspace (`split`).
+// forward rule picks at 768 x 8192 x 768.  Otherwise weight gradients whose
+// 32 x 96 grid fills whole rounds of the CUs (three quarters of each round
+// or more) take 32 x 96 tiles that load dY straight into the compute waves'
+// registers (LDS then holds the transposed A alone), whatever the
+// contraction: 23.2 against 24.9 us at 768 x 512 x 3072 (24.1 against 25.7
+// accumulating), 26.4 against 27.7 at 3072 x 512 x 768 with SwiGLU, 283
+// against 311 (48 x 48) at 768 x 8192 x 3072, 314 against 347 (96 x 96, which
+// combines G and U half as often as 48-wide tiles) at 3072 x 8192 x 768 with
+// SwiGLU, 558 against 608 at 768 x 16384 x 3072; at 1024 x 2048 x 1024, whose
+// 32 x 96 grid leaves most of a second round idle, 48.8 against 43.0.  A
+// transposed B takes 128 x 64 tiles where they come to two per CU and
+// 128 x 128 tiles do not: 74 against 80 us at 8192 x 768 x 768 and 282
+// against over 300 at 8192 x 3072 x 768.  The split-K tiles need the
+// caller's workspace (`split`).
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
     static const char *const fwd_mid = "64x64x64_w2x2_sp4_dAW", *const mid = "64x64x64_w2x2_sp4";
     static const char *const deep = "16x96x64_k4_sp8_pf3_il";
@@ -1383,16 +1380,14 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     // a transposed A takes 32 x 48 tiles where the rule takes 64 x 64
     // (whose backward form stages with registers)
     const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
-    if (op == kOpTN && swiglu && same_name(r, small) && K >= 4096 && ceil_div(M, 96) * ceil_div(N, 96) >= cus)
-        return bwd("96x96x64_w2x2_sp4_pf3_il_dA");
-    if (op == kOpTN && (same_name(r, small) || same_name(f, deep))) {
+    auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
+    const bool tn_small = op == kOpTN && (same_name(r, small) || same_name(f, deep));
+    if (tn_small) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
         if (t32 > cus && t32 < 2 * cus && t48 <= cus) return bwd("48x48x64_k4_sp4_pf3_dAW");
-        // long contractions whose output splits into whole 48 x 48 tiles
-        if (same_name(r, small) && K >= 4096 && M % 48 == 0 && N % 48 == 0 && t48 >= cus)
-            return bwd("48x48x64_k4_sp4_pf3_dAW");
-        if (same_name(r, small) && K < 4096 && ceil_div(M, 32) * ceil_div(N, 96) >= cus)
-            return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
+        // dY into registers where the 32 x 96 grid fills whole rounds
+        const int64_t t96 = ceil_div(M, 32) * ceil_div(N, 96);
+        if (t96 >= cus && fill(t96) >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
     }
     return bwd(r);
 }
