@@ -106,6 +106,12 @@ def test_config_table(lib):
     assert pick(2048, 768, 768, 0, 1) == "128x48x32_w2x1_k2_sp4_pf3_il_dA"
     assert pick(768, 768, 2048, 1, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert pick(1000, 768, 772, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    # large SwiGLU grids with fp32 W: 32 x 384 (32 x 192 where N is far
+    # from a multiple of 384), ahead of 128 x 128
+    assert pick(8192, 3072, 768, 1, 0) == "32x384x64_w1x4_sp4_pf3_il_dA_wr2"
+    assert pick(8192, 3072, 772, 1, 0) == "32x192x64_w1x4_sp4_pf3_il_dA_wr4"
+    assert pick(8192, 1536, 1536, 1, 0) == "32x384x64_w1x4_sp4_pf3_il_dA_wr2"
+    assert pick(8192, 1536, 1536, 1, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # without a workspace the long-K small grid does not split K; with fp32 W
     # a plain A does not split it either way
     assert pick(512, 3072, 768, 1, 0, ws=0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"

@@ -54,6 +54,8 @@ def test_forward_rule(M, K, N, w16, resid, tile):
     (200, 2500, 772, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (768, 768, 2048, True, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
     (1000, 768, 1532, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
+    (8192, 1024, 768, True, "32x384x64_w1x4_sp4_pf3_il_dA_wr2"),
+    (8191, 1024, 772, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (384, 2048, 768, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
 ])
 def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):

@@ -1134,6 +1134,7 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_dA_wr2"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
+    make_entry<Tile<32, 384, 64, 1, 4, 1, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("32x384x64_w1x4_sp4_pf3_il_dA_wr2"),
     // specialised, register staging only, two stages of loads in flight
     make_entry<Tile<128, 128, 32, 2, 2, 1, 4, 2, 1>>("128x128x32_w2x2_sp4"),
     // specialised, three stages in flight without the interleaving hint,
@@ -1231,7 +1232,13 @@ bool same_name(const char *a, const char *b) {
 // with the K range split over waves for small grids.  With SwiGLU, a
 // 64 x 384 tile re-stages (and recombines) each block of A rows half as
 // often as 128 x 192 at the same MFMA work per wave: 297 against 310 us at
-// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W.  Other grids
+// 8192 x 3072 x 768 with f16 W, 298 against 309 with fp32 W; with fp32 W,
+// 32 x 384 tiles with W in registers do better still (278 against 300 us
+// there, 280 against 311 and 352 for 128 x 128 at 8192 x 1536 x 1536, 1105
+// against 1220 and 1386 at 16384 x 3072 x 1536), and 32 x 192 ones where N
+// is far from a multiple of 384 (8191 x 3072 x 772: 361 against 409, and
+// 586 for 64 x 384; 8192 x 4096 x 2048: 1067 against 1090, and 1205 for
+// 128 x 128).  Other grids
 // too small for 128 x 128 take 128 x 64 tiles while those come to two per
 // CU: 512 x 768 x 8192 in 51.6 us against 56.8 for 64 x 64; 8192 x 768 x 768
 // in 77 against 86 us (f16 W) and 75 against 79 (fp32 W with R) for
@@ -1280,8 +1287,16 @@ bool same_name(const char *a, const char *b) {
 // backward table.
 const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward) {
     const int64_t cus = 256;
+    const bool wide_swiglu = swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus;
+    // SwiGLU with fp32 W on a large grid (ahead of 128 x 128, which combines
+    // each element of A once per 128 columns): 32 x 384 tiles with W in
+    // registers, or 32 x 192 where 384-wide tiles would leave more than a
+    // tenth of their columns past N
+    if (wide_swiglu && forward && !w16)
+        return ceil_div(N, 384) * 384 * 10 <= N * 11 ? "32x384x64_w1x4_sp4_pf3_il_dA_wr2"
+                                                      : "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
     if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
-    if (swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus) return "64x384x32_w1x4_sp8_pf4_il";
+    if (wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
     if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return "128x64x32_w2x2_sp4_pf3_il_dA";
