@@ -338,6 +338,7 @@ def test_backward_selection(lib):
     assert name(2, 512, 768, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(2, 512, 3072, 768) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(1, 512, 768, 16384) == "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"
+    assert name(1, 512, 768, 768) == "32x48x128_k4_sp8_pf2_dAW"
     assert name(1, 512, 3072, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(1, 512, 768, 3072) == "16x48x128_k4_sp4_dAW"
     assert name(2, 512, 768, 16384) == "128x128x32_w2x2_sp4_pf3_il_dA"

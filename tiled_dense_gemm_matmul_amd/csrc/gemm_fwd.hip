@@ -1180,6 +1180,8 @@ const ConfigEntry kBwdConfigs[] = {
     // a transposed B whose grid of 128 x 64 tiles comes to two per CU
     // (the 8192-token dX of the attention projections and of gate/up)
     make_bwd_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
+    // transposed B on the smallest grids: 128-deep slices two at a time
+    make_bwd_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp8_pf2_dAW"),
     // weight gradients over a short contraction: dY (B in its natural
     // layout) straight into the compute waves' registers
     make_bwd_entry<Tile<32, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
@@ -1397,6 +1399,9 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
     const bool tn_small = op == kOpTN && (same_name(r, small) || same_name(f, deep));
+    // a transposed B on the smallest grids: 128-deep slices, eight staging
+    // waves (qkvo dX, 512 x 768 x 768: 8.3 against 9.0 us for 64-deep ones)
+    if (op == kOpNT && same_name(r, small)) return bwd("32x48x128_k4_sp8_pf2_dAW");
     if (tn_small) {
         const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 48), t48 = ceil_div(M, 48) * ceil_div(N, 48);
         if (t32 > cus && t32 < 2 * cus && t48 <= cus) return bwd("48x48x64_k4_sp4_pf3_dAW");
