@@ -346,12 +346,28 @@ def test_backward_selection(lib):
     assert name(1, 8192, 768, 768) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 8192, 768, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 8192, 3072, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
-    assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
+    # dW over 1024 tokens or more onto at most two rounds of 48 x 48 tiles:
+    # those tiles, K split over two or four workgroups when there is a
+    # workspace, as far as each keeps 512 of the contraction and the grid
+    # stays within one workgroup per CU (two from 2048 tokens; a two-way
+    # split up to four from 8192)
+    assert name(2, 8192, 768, 768) == "48x48x64_k4_sp4_pf2_ks2_dAW"
+    assert name(2, 16384, 768, 768) == "48x48x64_k4_sp4_pf2_ks2_dAW"
+    assert name(2, 2048, 768, 768) == "48x48x64_k4_sp4_pf2_ks2_dAW"
+    assert name(2, 8192, 768, 768, ws=0) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 1024, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 1024, 512, 512) == "48x48x64_k4_sp4_pf2_ks2_dAW"
+    assert name(2, 2048, 512, 512) == "48x48x64_k4_sp4_pf2_ks4_dAW"
+    assert name(2, 8192, 384, 768) == "48x48x64_k4_sp4_pf2_ks4_dAW"
+    assert name(2, 8192, 512, 512, ws=0) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 2048, 1024, 1024) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 4096, 768, 1536) == "48x48x64_k4_sp4_pf3_dAW"
+    assert name(2, 8192, 1024, 1024) == "48x48x64_k4_sp4_pf2_ks2_dAW"
     # dW whose 32 x 96 grid fills whole rounds: dY into registers, whatever
     # the contraction
     assert name(2, 8192, 768, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(2, 8192, 1024, 4096) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
-    assert name(2, 2048, 1024, 1024) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert name(2, 512, 1024, 1024) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 8192, 3072, 768, 1, 1)).decode() == \
         "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(2, 512, 3072, 768, 1, 1)).decode() == \

@@ -90,19 +90,29 @@ def test_backward_matmul_t_128x64():
     _cmp(dX.cpu().numpy()[rows], ref, scale, "matmul_t 8192x768x768")
 
 
-@pytest.mark.parametrize("M,K,N", [(8192, 768, 768)])
-def test_backward_matmul_at_48x48_long_contraction(M, K, N):
-    # dW = X^T @ dY over 8192 tokens: 768 x 768 (too large for the split-K
-    # workspace; 256 tiles of 48 x 48, one round)
+@pytest.mark.parametrize("M,K,N,ks", [(8192, 768, 768, 2), (2051, 760, 764, 2), (4099, 508, 516, 4)])
+def test_backward_matmul_at_48x48_long_contraction(M, K, N, ks):
+    # dW = X^T @ dY over 2048 tokens or more onto a small grid of 48 x 48
+    # tiles: K split over ks workgroups with a workspace (ragged splits where
+    # the token count is), the whole K per workgroup without one; both
+    # against the oracle, and accumulating into dW0 with the split
     import torch
     from tiled_dense_gemm_matmul_amd import binding
-    assert binding.bwd_kernel_config("matmul_at", M, K, N) == "48x48x64_k4_sp4_pf3_dAW"
     c = inputs.backward_case(12 + N, M, K, N)
-    dW = binding.matmul_at(to_dev(c["X"]), to_dev(c["dY"]))
-    torch.cuda.synchronize()
+    X, dY = to_dev(c["X"]), to_dev(c["dY"])
     rows = _rows(K, 9, count=32, tail=48)
     ref, scale = oracle.matmul_at(c["X"], c["dY"], rows=rows, want_scale=True)
-    _cmp(dW.cpu().numpy()[rows], ref, scale, f"matmul_at {M}x{K}x{N}")
+    for ws, tile in ((True, f"48x48x64_k4_sp4_pf2_ks{ks}_dAW"), (False, "48x48x64_k4_sp4_pf3_dAW")):
+        assert binding.bwd_kernel_config("matmul_at", M, K, N, workspace=ws) == tile
+        dW = binding.matmul_at(X, dY, use_workspace=ws)
+        torch.cuda.synchronize()
+        _cmp(dW.cpu().numpy()[rows], ref, scale, f"matmul_at {M}x{K}x{N} {tile}")
+    dW0 = inputs.backward_case(13 + N, M, K, N, acc=True)["dW0"]
+    out = to_dev(dW0)
+    binding.matmul_at(X, dY, out=out, acc=True)
+    torch.cuda.synchronize()
+    ref, scale = oracle.matmul_at(c["X"], c["dY"], Y0=dW0, rows=rows, want_scale=True)
+    _cmp(out.cpu().numpy()[rows], ref, scale, f"matmul_at_acc {M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("tokens", [512, 8192])
