@@ -99,7 +99,18 @@ def test_config_table(lib):
     assert pick(512, 768, 768, 0, 1) == "32x48x128_k4_sp8_pf2_dAW"
     assert pick(512, 1024, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     assert pick(512, 1536, 768, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
-    assert pick(128, 3072, 768, 1, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(128, 3072, 768, 1, 0, ws=0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    # small outputs over a long contraction with fp32 W and a workspace: the
+    # 16-row tile and two- or four-way K split of least estimated time
+    assert pick(128, 3072, 768, 1, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"
+    assert pick(64, 3072, 768, 1, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
+    assert pick(256, 3072, 768, 1, 0) == "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"
+    assert pick(128, 8192, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
+    assert pick(512, 8192, 512, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"
+    assert pick(128, 8192, 768, 0, 0, ws=0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    # below 3072 of contraction only grids of at most half a round split
+    assert pick(64, 2048, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
+    assert pick(128, 2048, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     assert pick(256, 768, 1024, 1, 0) == "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
     # mid-size fp32 grids: 32 x 192 on whole rounds, else 16 x 96 / 16 x 48
     assert pick(2048, 768, 768, 0, 0) == "32x192x64_w1x4_sp4_pf3_il_dA_wr4"

@@ -70,6 +70,38 @@ def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):
     check(c, y.cpu().numpy(), label=f"{M}x{K}x{N} {tile}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu,tile", [
+    (77, 4100, 500, False, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"),
+    (63, 3076, 2044, False, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"),
+    (29, 3072, 2044, True, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"),
+    (175, 3076, 1020, True, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"),
+    (61, 3076, 2044, True, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"),
+])
+def test_forward_split_small_outputs(M, K, N, swiglu, tile):
+    # small outputs over a long contraction with fp32 W: 16-row tiles with W
+    # in registers and K split over two or four workgroups when there is a
+    # workspace (the whole K without one); both choices on every element
+    # against the oracle, the split one run twice and bitwise equal
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.kernel_config(M, K, N, swiglu=swiglu) == tile
+    assert "_ks" not in binding.kernel_config(M, K, N, swiglu=swiglu, workspace=False)
+    c = inputs.random_case(3000 + M + N, M, K, N, swiglu=swiglu, residual=swiglu, gate_scale=3.0)
+    d = {k: to_dev(v) for k, v in c.items()}
+    ys = []
+    for ws in (True, True, False):
+        if swiglu:
+            y = binding.matmul_residual_swiglu_a(d["G"], d["U"], d["W"], d["R"], use_workspace=ws)
+        else:
+            y = binding.matmul(d["X"], d["W"], use_workspace=ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    say(f"forward {'SwiGLU ' if swiglu else ''}{M}x{K}x{N} -> {tile}")
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+    check(c, ys[0], label=f"{M}x{K}x{N} {tile}")
+    check(c, ys[2], label=f"{M}x{K}x{N} without a workspace")
+
+
 def _cmp(y, ref, scale, label):
     res = oracle.compare(y, ref, scale, oracle.TOL_W32)
     say(f"  {label}: max err/tol {res['max_ratio']:.4g}, fails {res['fails']} of {res['n']}")

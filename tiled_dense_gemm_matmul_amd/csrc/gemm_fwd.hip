@@ -1133,6 +1133,13 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 2, 1, 1, 1, 0, 2, 0, 4>>("16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
     make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    // the same tiles with K split over two or four workgroups (small
+    // outputs over a long contraction)
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 2, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 3, 1, 1, 4, 0, 2, 1, 2>>("16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"),
+    make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 2, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"),
+    make_entry<Tile<16, 96, 128, 1, 2, 2, 4, 3, 1, 1, 4, 0, 2, 1, 4>>("16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"),
+    make_entry<Tile<16, 192, 128, 1, 4, 1, 4, 3, 1, 1, 4, 0, 2, 0, 4>>("16x192x128_w1x4_sp4_pf3_il_ks4_wr4"),
     make_entry<Tile<32, 192, 64, 1, 4, 1, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     make_entry<Tile<32, 384, 64, 1, 4, 1, 4, 3, 1, 1, 1, 0, 2, 1, 2>>("32x384x64_w1x4_sp4_pf3_il_dA_wr2"),
     // specialised, register staging only, two stages of loads in flight
@@ -1324,11 +1331,51 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
         // 16 x 48 where its grid fills whole rounds better (with SwiGLU,
         // which it combines twice as often, only below one round of 16 x 96)
         const int64_t s96 = ceil_div(M, 16) * ceil_div(N, 96), s48 = ceil_div(M, 16) * ceil_div(N, 48);
-        if (fill(s96) < fill(s48) && (!swiglu || s96 < cus)) return "16x48x128_k4_sp4_pf3_il_dA_wr2";
-        // SwiGLU on one round at most: eight staging waves; otherwise four,
-        // which lets two workgroups share a CU
-        if (swiglu && s96 <= cus) return "16x96x128_w1x2_k2_sp8_pf2_il_wr4";
-        return "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
+        const char *base = fill(s96) < fill(s48) && (!swiglu || s96 < cus) ? "16x48x128_k4_sp4_pf3_il_dA_wr2"
+                           // SwiGLU on one round at most: eight staging
+                           // waves; otherwise four, which lets two
+                           // workgroups share a CU
+                           : swiglu && s96 <= cus ? "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
+                                                  : "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
+        // Over a long contraction with a workspace, the 16-row tile and K
+        // split (none, two or four workgroups, each keeping 512 or more of
+        // the contraction, 1024 or more where the split grid exceeds two
+        // workgroups per CU, the partial tiles within 2^20 elements) of least
+        // estimated time: the rounds of workgroups over the CUs, times each
+        // one's contraction, times its width in 48-column units (plus half a
+        // unit for the SwiGLU combine, done once per tile), and 1.2 times
+        // that for 16 x 48 tiles alone on their CUs (24 MFMAs per wave
+        // between barriers, with no second workgroup to fill the waits).
+        // Ties keep the choice above.  Not below 3072 for grids of more than
+        // half a round (splits there lost up to 18%), nor below 8192 for the
+        // eight-staging-wave SwiGLU tile (0.81 to 1.14 times as fast).
+        // Against the choice above, over 16 to 768 rows, contractions of
+        // 2048 to 16384 and 512 to 2048 columns: 1.6 times as fast on the
+        // geometric mean, up to 3.4 (64 x 3072 x 768 with SwiGLU
+        // 17.2 -> 8.3 us, 128 x 8192 x 768 37 -> 18 us).
+        const bool base48 = same_name(base, "16x48x128_k4_sp4_pf3_il_dA_wr2");
+        const bool sp8 = same_name(base, "16x96x128_w1x2_k2_sp8_pf2_il_wr4");
+        if (!split || K < (sp8 ? 8192 : 2048) || (K < 3072 && (base48 ? s48 : s96) > cus / 2)) return base;
+        struct Cand { int bn, ks; const char *name; };
+        static const Cand cands[] = {
+            {48, 1, "16x48x128_k4_sp4_pf3_il_dA_wr2"},         {96, 1, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"},
+            {48, 2, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"},     {96, 2, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"},
+            {192, 2, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"},    {48, 4, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"},
+            {96, 4, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"}, {192, 4, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"}};
+        auto cost = [&](int bn, int ks) {
+            const int64_t wgs = ceil_div(M, 16) * ceil_div(N, bn) * ks;
+            return (double)ceil_div(wgs, cus) * (double)ceil_div(K, ks) * (bn / 48.0 + (swiglu ? 0.5 : 0.0)) *
+                   (bn == 48 && wgs <= cus ? 1.2 : 1.0);
+        };
+        const char *best = base;
+        double best_cost = cost(base48 ? 48 : 96, 1);
+        for (const Cand &c : cands) {
+            const int64_t wgs = ceil_div(M, 16) * ceil_div(N, c.bn) * c.ks;
+            if (c.ks > 1 && (K / c.ks < (wgs > 2 * cus ? 1024 : 512) || c.ks * M * N > ((int64_t)1 << 20))) continue;
+            const double t = cost(c.bn, c.ks);
+            if (t < best_cost) best = c.name, best_cost = t;
+        }
+        return best;
     }
     // forward products: 128 x 48 where that grid fills the CUs, which stages
     // (and widens, or combines) each block of W (or A) half as often
@@ -1367,8 +1414,9 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // lm_head's dX, 512 x 16384 x 768).  Where those 32 x 48 tiles of a
 // transposed A come to between one and two per CU while 48 x 48 tiles come
 // to at most one, the 48 x 48 tiles finish in one round: 9.7 against 10.8 us
-// at 768 x 512 x 768, and 98 against over 125 us for the 16 x 96 tiles the
-// forward rule picks at 768 x 8192 x 768.  Otherwise weight gradients whose
+// at 768 x 512 x 768.  Over a contraction of 1024 or more, grids of up to
+// two rounds of 48 x 48 tiles take those tiles with K split over two or
+// four workgroups (below).  Otherwise weight gradients whose
 // 32 x 96 grid fills whole rounds of the CUs (three quarters of each round
 // or more) take 32 x 96 tiles that load dY straight into the compute waves'
 // registers (LDS then holds the transposed A alone), whatever the
