@@ -108,6 +108,11 @@ def test_config_table(lib):
     assert pick(128, 8192, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
     assert pick(512, 8192, 512, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"
     assert pick(128, 8192, 768, 0, 0, ws=0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    # the same for binary16 W over the LDS-staged tiles
+    assert pick(64, 3072, 768, 1, 1) == "16x48x128_k4_sp4_ks4_dAW"
+    assert pick(128, 8192, 768, 0, 1) == "32x48x128_k4_sp8_pf2_ks4_dAW"
+    assert pick(256, 3072, 768, 1, 1) == "32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"
+    assert pick(128, 8192, 768, 0, 1, ws=0) == "16x48x128_k4_sp4_dAW"
     # below 3072 of contraction only grids of at most half a round split
     assert pick(64, 2048, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
     assert pick(128, 2048, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"

@@ -55,7 +55,7 @@ def test_empty_outputs():
     assert b.matmul(X, W).shape == (5, 0)
 
 
-@pytest.mark.parametrize("cfg", [None] + list(range(32)))
+@pytest.mark.parametrize("cfg", [None] + list(range(40)))
 def test_integer_inputs_bit_exact(cfg):
     b = _lib()
     if cfg is not None and cfg >= b.num_configs():

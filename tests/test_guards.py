@@ -68,7 +68,7 @@ def _fwd_configs():
     return binding.num_configs()
 
 
-@pytest.mark.parametrize("cfg", [None] + list(range(32)))
+@pytest.mark.parametrize("cfg", [None] + list(range(40)))
 def test_forward_every_config(cfg):
     from tiled_dense_gemm_matmul_amd import binding
     if cfg is not None and cfg >= binding.num_configs():

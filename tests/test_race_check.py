@@ -74,7 +74,7 @@ def _same(a, b, label):
     assert eq, label
 
 
-@pytest.mark.parametrize("cfg", list(range(32)))
+@pytest.mark.parametrize("cfg", list(range(40)))
 def test_forward_configs(cfg):
     binding, lib, _ = _libs()
     if cfg >= lib.gemm_num_configs():

@@ -70,23 +70,29 @@ def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):
     check(c, y.cpu().numpy(), label=f"{M}x{K}x{N} {tile}")
 
 
-@pytest.mark.parametrize("M,K,N,swiglu,tile", [
-    (77, 4100, 500, False, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"),
-    (63, 3076, 2044, False, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"),
-    (29, 3072, 2044, True, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"),
-    (175, 3076, 1020, True, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"),
-    (61, 3076, 2044, True, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"),
+@pytest.mark.parametrize("M,K,N,swiglu,w16,tile", [
+    (77, 4100, 500, False, False, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"),
+    (63, 3076, 2044, False, False, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"),
+    (29, 3072, 2044, True, False, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"),
+    (175, 3076, 1020, True, False, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"),
+    (61, 3076, 2044, True, False, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"),
+    # binary16 W: LDS-staged tiles
+    (77, 3076, 2044, False, True, "16x48x128_k4_sp4_ks2_dAW"),
+    (17, 3076, 500, True, True, "16x48x128_k4_sp4_ks4_dAW"),
+    (255, 3076, 2044, True, True, "32x48x128_k4_sp8_pf2_ks2_dAW"),
+    (17, 3076, 2044, False, True, "32x48x128_k4_sp8_pf2_ks4_dAW"),
+    (45, 3076, 2044, True, True, "32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"),
 ])
-def test_forward_split_small_outputs(M, K, N, swiglu, tile):
-    # small outputs over a long contraction with fp32 W: 16-row tiles with W
-    # in registers and K split over two or four workgroups when there is a
-    # workspace (the whole K without one); both choices on every element
-    # against the oracle, the split one run twice and bitwise equal
+def test_forward_split_small_outputs(M, K, N, swiglu, w16, tile):
+    # small outputs over a long contraction: the 16- or 32-row tiles with K
+    # split over two or four workgroups when there is a workspace (the whole
+    # K without one); both choices on every element against the oracle, the
+    # split one run twice and bitwise equal
     import torch
     from tiled_dense_gemm_matmul_amd import binding
-    assert binding.kernel_config(M, K, N, swiglu=swiglu) == tile
-    assert "_ks" not in binding.kernel_config(M, K, N, swiglu=swiglu, workspace=False)
-    c = inputs.random_case(3000 + M + N, M, K, N, swiglu=swiglu, residual=swiglu, gate_scale=3.0)
+    assert binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16) == tile
+    assert "_ks" not in binding.kernel_config(M, K, N, swiglu=swiglu, w16=w16, workspace=False)
+    c = inputs.random_case(3000 + M + N, M, K, N, swiglu=swiglu, w16=w16, residual=swiglu, gate_scale=3.0)
     d = {k: to_dev(v) for k, v in c.items()}
     ys = []
     for ws in (True, True, False):

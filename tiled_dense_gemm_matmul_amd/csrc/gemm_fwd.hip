@@ -1128,6 +1128,13 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 3>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"),
     make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 2, 1, 2, 2>>("32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW"),
     make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 1, 0, 2, 3>>("16x48x128_k4_sp4_dAW"),
+    // small grids with binary16 W over a long contraction: K split over two
+    // or four workgroups
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 2, 0, 2, 3>>("16x48x128_k4_sp4_ks2_dAW"),
+    make_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 4, 0, 2, 3>>("16x48x128_k4_sp4_ks4_dAW"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 2, 0, 2, 3>>("32x48x128_k4_sp8_pf2_ks2_dAW"),
+    make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 4, 0, 2, 3>>("32x48x128_k4_sp8_pf2_ks4_dAW"),
+    make_entry<Tile<32, 96, 128, 1, 2, 2, 8, 3, 1, 1, 4, 1, 2, 3>>("32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"),
     // W in the compute waves' registers (fp32 W only)
     make_entry<Tile<16, 192, 128, 1, 4, 1, 4, 3, 1, 1, 2, 0, 2, 0, 4>>("16x192x128_w1x4_sp4_pf3_il_ks2_wr4"),
     make_entry<Tile<16, 96, 128, 1, 2, 2, 8, 2, 1, 1, 1, 0, 2, 0, 4>>("16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
@@ -1381,17 +1388,61 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     // (and widens, or combines) each block of W (or A) half as often
     if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
     if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
-    if (M <= 128) return "16x48x128_k4_sp4_dAW";
-    if (K >= 2048) {
+    const char *small = nullptr;
+    if (M <= 128) small = "16x48x128_k4_sp4_dAW";
+    else if (K >= 2048) {
         // long K on a small grid: split K in two when there is a workspace
         // (for outputs up to 2^19 elements, the range measured)
         if (split && M * N <= kSplitMaxElems && ceil_div(M, 32) * ceil_div(N, 96) * 2 >= cus) {
             if (!forward) return "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW";
-            return swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW";
+            small = swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW";
+        } else {
+            small = forward ? "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW" : "16x96x64_k4_sp8_pf3_il";
         }
-        return forward ? "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW" : "16x96x64_k4_sp8_pf3_il";
+    } else {
+        small = forward ? "32x48x128_k4_sp8_pf2_dAW" : "32x48x64_k4_sp4_pf3_dAW";
     }
-    return forward ? "32x48x128_k4_sp8_pf2_dAW" : "32x48x64_k4_sp4_pf3_dAW";
+    if (!forward || !split || K < 2048) return small;
+    // The forward products with binary16 W over a long contraction with a
+    // workspace: the tile and K split of least estimated time, as for fp32
+    // W above, with the work in units of 16 x 48 outputs (and the SwiGLU
+    // combine, done once per tile row, in half units per 16 rows).  Ties keep
+    // the choice above.  64 x 3072 x 768 with SwiGLU: 21.5 -> 9.7 us;
+    // 128 x 8192 x 768: 42.9 -> 20.2 us; 32 x 4096 x 1024: 22.4 -> 9.8 us.
+    // (SwiGLU takes the 32 x 96 two-way split in its W-only DMA form, as
+    // above)
+    const char *const split96 =
+        swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW";
+    struct Cand { int bm, bn, ks; const char *name; };
+    // (in this order, so that among equal estimates the first, with fewer
+    // and larger workgroups, is taken)
+    const Cand cands[] = {
+        {32, 48, 1, "32x48x128_k4_sp8_pf2_dAW"},     {32, 48, 2, "32x48x128_k4_sp8_pf2_ks2_dAW"},
+        {32, 48, 4, "32x48x128_k4_sp8_pf2_ks4_dAW"}, {16, 48, 1, "16x48x128_k4_sp4_dAW"},
+        {16, 48, 2, "16x48x128_k4_sp4_ks2_dAW"},     {16, 48, 4, "16x48x128_k4_sp4_ks4_dAW"},
+        {16, 96, 1, "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"},
+        {32, 96, 2, split96},
+        {32, 96, 4, "32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"}};
+    auto grid = [&](const Cand &c) { return ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.ks; };
+    auto cost = [&](const Cand &c) {
+        const int64_t wgs = grid(c);
+        return (double)ceil_div(wgs, cus) * (double)ceil_div(K, c.ks) *
+               (c.bm * c.bn / 768.0 + (swiglu ? c.bm / 32.0 : 0.0)) *
+               (c.bm == 16 && c.bn == 48 && wgs <= cus ? 1.2 : 1.0);
+    };
+    const Cand *base = nullptr;
+    for (const Cand &c : cands)
+        if (same_name(c.name, small)) base = &c;
+    if (base == nullptr || (K < 3072 && grid(*base) / base->ks > cus / 2)) return small;
+    const char *best = small;
+    double best_cost = cost(*base);
+    for (const Cand &c : cands) {
+        const int64_t wgs = grid(c);
+        if (c.ks > 1 && (K / c.ks < (wgs > 2 * cus ? 1024 : 512) || c.ks * M * N > ((int64_t)1 << 20))) continue;
+        const double t = cost(c);
+        if (t < best_cost) best = c.name, best_cost = t;
+    }
+    return best;
 }
 
 // The forward choice: an index into kConfigs (-1 if the rule names a tile
