@@ -345,7 +345,15 @@ def test_backward_selection(lib):
     def name(op, *shape, ws=1):
         return lib.gemm_bwd_config_name(lib.gemm_bwd_select_config(op, *shape, 0, ws)).decode()
     # without a workspace the lm_head's input gradient does not split K
-    assert name(1, 512, 768, 16384, ws=0) == "16x96x64_k4_sp8_pf3_il"
+    assert name(1, 512, 768, 16384, ws=0) == "32x48x128_k4_sp8_pf2_dAW"
+    # a transposed B over a long contraction onto a small grid: 32 x 48 or
+    # 16 x 48 tiles, K split with a workspace (from 2048 on grids of at most
+    # half a round, from 8192 beyond)
+    assert name(1, 64, 768, 16384) == "32x48x128_k4_sp8_pf2_ks8_dAW"
+    assert name(1, 128, 768, 16384) == "32x48x128_k4_sp8_pf2_ks4_dAW"
+    assert name(1, 256, 768, 16384) == "32x48x128_k4_sp8_pf2_ks2_dAW"
+    assert name(1, 256, 768, 16384, ws=0) == "16x48x128_k4_sp4_dAW"
+    assert name(1, 256, 768, 3072) == "16x48x128_k4_sp4_dAW"
     # dW of the 768 x 768 projections: 384 tiles of 32 x 48 would take two
     # rounds on 256 CUs, 256 tiles of 48 x 48 take one
     assert name(2, 512, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"

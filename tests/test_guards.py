@@ -97,7 +97,7 @@ def test_forward_every_config(cfg):
 BWD_OPS = ["t", "t_acc", "at", "at_acc", "at_swiglu", "at_acc_swiglu"]
 
 
-@pytest.mark.parametrize("cfg", [None] + list(range(16)))
+@pytest.mark.parametrize("cfg", [None] + list(range(24)))
 def test_backward_every_config(cfg):
     """matmul_t: dX [292 x 68] over a 292-long contraction; matmul_at: dW
     [68 x 292] over 292 rows; with and without accumulation, and with the
@@ -126,7 +126,7 @@ def test_backward_every_config(cfg):
         check_bwd(c, op, yy, label=name)
 
 
-@pytest.mark.parametrize("cfg", [None] + list(range(16)))
+@pytest.mark.parametrize("cfg", [None] + list(range(24)))
 def test_fused_swiglu_backward_every_config(cfg):
     """dGATE, dUP from dH = dY W^T in matmul_t's epilogue: GATE and UP read
     there (poisoned neighbours), both gradients banded."""

@@ -92,7 +92,7 @@ def test_forward_configs(cfg):
             _same(a, b, f"{name} {M}x{K}x{N} swiglu={swiglu} w16={w16}")
 
 
-@pytest.mark.parametrize("cfg", list(range(16)))
+@pytest.mark.parametrize("cfg", list(range(24)))
 def test_backward_configs(cfg):
     import torch
     binding, lib, slib = _libs()

@@ -114,6 +114,43 @@ def _cmp(y, ref, scale, label):
     assert res["fails"] == 0, res
 
 
+@pytest.mark.parametrize("M,K,N,tile", [
+    (175, 1020, 8196, "16x48x128_k4_sp4_ks2_dAW"),
+    (17, 500, 2052, "16x48x128_k4_sp4_ks4_dAW"),
+    (17, 500, 4100, "16x48x128_k4_sp4_ks8_dAW"),
+    (131, 1020, 8196, "32x48x128_k4_sp8_pf2_ks2_dAW"),
+    (45, 1020, 2052, "32x48x128_k4_sp8_pf2_ks4_dAW"),
+    (17, 772, 4100, "32x48x128_k4_sp8_pf2_ks8_dAW"),
+])
+def test_backward_matmul_t_split_small_outputs(M, K, N, tile):
+    # dX = dY @ W^T over a long contraction onto a small grid: K split over
+    # two, four or eight workgroups with a workspace (not without one); both
+    # against the oracle, the split one twice and bitwise equal; then the
+    # same split with the SwiGLU backward in its epilogue (after the
+    # reduction) against the composition of the two oracles
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    from test_backward import check_fused, fused_ref
+    assert binding.bwd_kernel_config("matmul_t", M, K, N) == tile
+    assert "_ks" not in binding.bwd_kernel_config("matmul_t", M, K, N, workspace=False)
+    c = inputs.backward_case(40 + M + N, M, K, N, swiglu=True, gate_scale=3.0)
+    dY, W = to_dev(c["dY"]), to_dev(c["W"])
+    ys = []
+    for ws in (True, True, False):
+        y = binding.matmul_t(dY, W, use_workspace=ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+    ref, scale = oracle.matmul_t(c["dY"], c["W"], want_scale=True)
+    _cmp(ys[0], ref, scale, f"matmul_t {M}x{K}x{N} {tile}")
+    _cmp(ys[2], ref, scale, f"matmul_t {M}x{K}x{N} without a workspace")
+    dg, du = binding.matmul_t_swiglu_backward(dY, W, to_dev(c["G"]), to_dev(c["U"]))
+    torch.cuda.synchronize()
+    rg, ru, bg, bu = fused_ref(c, c["G"], c["U"])
+    check_fused(dg.cpu().numpy(), rg, bg, "dGATE")
+    check_fused(du.cpu().numpy(), ru, bu, "dUP")
+
+
 def test_backward_matmul_t_128x64():
     # dX = dY @ W^T for 8192 tokens, 768 outputs, 768 inputs
     import torch

@@ -1201,6 +1201,14 @@ const ConfigEntry kBwdConfigs[] = {
     make_bwd_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     // transposed B on the smallest grids: 128-deep slices two at a time
     make_bwd_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp8_pf2_dAW"),
+    // a transposed B over a long contraction onto a small grid: K split
+    // over two, four or eight workgroups
+    make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 2, 0, 2, 3>>("16x48x128_k4_sp4_ks2_dAW"),
+    make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 4, 0, 2, 3>>("16x48x128_k4_sp4_ks4_dAW"),
+    make_bwd_entry<Tile<16, 48, 128, 1, 1, 4, 4, 2, 1, 0, 8, 0, 2, 3>>("16x48x128_k4_sp4_ks8_dAW"),
+    make_bwd_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 2, 0, 2, 3>>("32x48x128_k4_sp8_pf2_ks2_dAW"),
+    make_bwd_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 4, 0, 2, 3>>("32x48x128_k4_sp8_pf2_ks4_dAW"),
+    make_bwd_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 8, 0, 2, 3>>("32x48x128_k4_sp8_pf2_ks8_dAW"),
     // weight gradients over a short contraction: dY (B in its natural
     // layout) straight into the compute waves' registers
     make_bwd_entry<Tile<32, 96, 128, 1, 2, 2, 4, 3, 1, 1, 1, 0, 2, 1, 4>>("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
@@ -1481,7 +1489,7 @@ int select_config(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool spl
 // 128 x 128 tiles do not: 74 against 80 us at 8192 x 768 x 768 and 282
 // against over 300 at 8192 x 3072 x 768.  The split-K tiles need the
 // caller's workspace (`split`).
-int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
+int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
     static const char *const fwd_mid = "64x64x64_w2x2_sp4_dAW", *const mid = "64x64x64_w2x2_sp4";
     static const char *const deep = "16x96x64_k4_sp8_pf3_il";
     static const char *const deep_split = "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW";
@@ -1540,6 +1548,57 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
         if (t96 >= cus && fill(t96) >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
     }
     return bwd(r);
+}
+
+// A transposed B (matmul_t) over a contraction of 2048 or more, where the
+// rule above lands on one of its small-grid tiles: the 32 x 48 or 16 x 48
+// tile and K split (none, or with a workspace two, four or eight
+// workgroups) of least estimated time, as for the forward products (the
+// rounds of workgroups over the CUs, times each one's contraction, times its
+// area in 16 x 48 units, 1.2 times that for 16 x 48 tiles alone on their
+// CUs; each split keeps 512 or more of the contraction, 1024 or more past two
+// workgroups per CU, the grid stays within six per CU and the partial tiles
+// within 2^20 elements; ties keep the rule's tile).  Splits only from 8192
+// where the 16 x 48 grid exceeds half a round: below that they measured up
+// to 15% slower.  The rule's 16 x 96 x 64 tile never stays: for a transposed
+// B it measured 2 to 2.4 times as slow as 16 x 48 tiles everywhere.  dX over
+// 64 tokens of the lm_head (64 x 16384 x 768): 64.5 -> 20.1 us; over 256
+// tokens, with or without a workspace: 159 -> 60 or 66 us.
+int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
+    const int r = select_bwd_rule(op, M, K, N, swiglu, split);
+    if (op != kOpNT || K < 2048 || r < 0) return r;
+    const ConfigEntry &e = kBwdConfigs[r];
+    const bool deep = same_name(e.name, "16x96x64_k4_sp8_pf3_il");
+    static const char *const small_tiles[] = {"16x48x128_k4_sp4_dAW", "32x48x128_k4_sp8_pf2_dAW",
+                                              "32x96x64_w1x2_k2_sp8_pf3_il_ks2_cil_dW",
+                                              "128x96x64_w2x2_sp8_pf3_il_ks8_cil_dA"};
+    bool small = deep;
+    for (const char *t : small_tiles) small = small || same_name(e.name, t);
+    if (!small) return r;
+    const int64_t cus = 256;
+    auto cost = [&](int bm, int bn, int ks) {
+        const int64_t wgs = ceil_div(M, bm) * ceil_div(N, bn) * ks;
+        return (double)ceil_div(wgs, cus) * (double)ceil_div(K, ks) * (bm * bn / 768.0) *
+               (bm == 16 && bn == 48 && wgs <= cus ? 1.2 : 1.0);
+    };
+    const bool splits = split && K >= (ceil_div(M, 16) * ceil_div(N, 48) > cus / 2 ? 8192 : 2048);
+    struct Cand { int bm, bn, ks; const char *name; };
+    static const Cand cands[] = {
+        {32, 48, 1, "32x48x128_k4_sp8_pf2_dAW"},     {32, 48, 2, "32x48x128_k4_sp8_pf2_ks2_dAW"},
+        {32, 48, 4, "32x48x128_k4_sp8_pf2_ks4_dAW"}, {32, 48, 8, "32x48x128_k4_sp8_pf2_ks8_dAW"},
+        {16, 48, 1, "16x48x128_k4_sp4_dAW"},         {16, 48, 2, "16x48x128_k4_sp4_ks2_dAW"},
+        {16, 48, 4, "16x48x128_k4_sp4_ks4_dAW"},     {16, 48, 8, "16x48x128_k4_sp4_ks8_dAW"}};
+    int best = r;
+    double best_cost = deep ? 1e300 : cost(e.bm, e.bn, e.ks);
+    for (const Cand &c : cands) {
+        const int64_t wgs = ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.ks;
+        if (c.ks > 1 && (!splits || K / c.ks < (wgs > 2 * cus ? 1024 : 512) || wgs > 6 * cus ||
+                         c.ks * M * N > ((int64_t)1 << 20)))
+            continue;
+        const double t = cost(c.bm, c.bn, c.ks);
+        if (t < best_cost) best = table_index(kBwdConfigs, kNumBwdConfigs, c.name), best_cost = t;
+    }
+    return best;
 }
 
 // ---------------------------------------------------------------------------
