@@ -1257,6 +1257,43 @@ bool same_name(const char *a, const char *b) {
     return *a == 0 && *b == 0;
 }
 
+// Choosing among tiles and K splits by estimated time (small outputs over a
+// long contraction).  The estimate: the rounds of workgroups over the 256
+// CUs, times each workgroup's contraction, times its area in units of
+// 16 x 48 outputs (plus, with SwiGLU, half a unit per 16 rows for the
+// combine, done once per tile), and 1.2 times that for 16 x 48 tiles alone
+// on their CUs (24 MFMAs per wave between barriers, with no second
+// workgroup to fill the waits).  A split keeps 512 or more of the
+// contraction per workgroup (1024 or more where the split grid exceeds two
+// workgroups per CU), at most max_wgs workgroups and 2^20 partial elements.
+// Ties keep `base` (a negative base_cost: the base never stays); among
+// candidates of equal estimate the first listed wins.
+struct SplitCand { int bm, bn, ks; const char *name; };
+
+double split_estimate(int64_t M, int64_t K, int64_t N, bool swiglu, int bm, int bn, int ks) {
+    const int64_t cus = 256;
+    const int64_t wgs = ceil_div(M, bm) * ceil_div(N, bn) * ks;
+    return (double)ceil_div(wgs, cus) * (double)ceil_div(K, ks) * (bm * bn / 768.0 + (swiglu ? bm / 32.0 : 0.0)) *
+           (bm == 16 && bn == 48 && wgs <= cus ? 1.2 : 1.0);
+}
+
+const char *pick_by_estimate(int64_t M, int64_t K, int64_t N, bool swiglu, bool splits, int64_t max_wgs,
+                             const SplitCand *cands, int count, const char *base, double base_cost) {
+    const int64_t cus = 256;
+    const char *best = base;
+    double best_cost = base_cost < 0 ? 1e300 : base_cost;
+    for (int i = 0; i < count; ++i) {
+        const SplitCand &c = cands[i];
+        const int64_t wgs = ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.ks;
+        if (c.ks > 1 && (!splits || K / c.ks < (wgs > 2 * cus ? 1024 : 512) || wgs > max_wgs ||
+                         c.ks * M * N > ((int64_t)1 << 20)))
+            continue;
+        const double t = split_estimate(M, K, N, swiglu, c.bm, c.bn, c.ks);
+        if (t < best_cost) best = c.name, best_cost = t;
+    }
+    return best;
+}
+
 // Tile choice from the output grid, measured on MI355X: the largest tile
 // that still gives every CU work for the whole kernel, then narrower tiles
 // with the K range split over waves for small grids.  With SwiGLU, a
@@ -1309,8 +1346,9 @@ bool same_name(const char *a, const char *b) {
 // 16 x 96 tiles use eight staging waves up to one round (24.9 against 26.6 us
 // at 512 x 3072 x 768 without a workspace) and four beyond, where two
 // workgroups then share a CU (2000 x 1000 x 780: 40.6 against 44.8).  A
-// plain A is never split over workgroups (512 x 3072 x 768: 20.8 us for
-// 16 x 96 against 21.9 for the fastest split).
+// plain A at 512 x 3072 x 768 is not split over workgroups (20.8 us for
+// 16 x 96 against 21.9 for the fastest split); smaller outputs over long
+// contractions are (pick_by_estimate, below).
 // `forward` false: the rule as the backward products measured it, without
 // the 128 x 64 and 128 x 48 tiles, the whole-round 64 x 64 choice, the
 // 128-deep slices and W in registers; every name it gives is in the
@@ -1352,45 +1390,25 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
                            // workgroups share a CU
                            : swiglu && s96 <= cus ? "16x96x128_w1x2_k2_sp8_pf2_il_wr4"
                                                   : "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4";
-        // Over a long contraction with a workspace, the 16-row tile and K
-        // split (none, two or four workgroups, each keeping 512 or more of
-        // the contraction, 1024 or more where the split grid exceeds two
-        // workgroups per CU, the partial tiles within 2^20 elements) of least
-        // estimated time: the rounds of workgroups over the CUs, times each
-        // one's contraction, times its width in 48-column units (plus half a
-        // unit for the SwiGLU combine, done once per tile), and 1.2 times
-        // that for 16 x 48 tiles alone on their CUs (24 MFMAs per wave
-        // between barriers, with no second workgroup to fill the waits).
-        // Ties keep the choice above.  Not below 3072 for grids of more than
-        // half a round (splits there lost up to 18%), nor below 8192 for the
-        // eight-staging-wave SwiGLU tile (0.81 to 1.14 times as fast).
-        // Against the choice above, over 16 to 768 rows, contractions of
-        // 2048 to 16384 and 512 to 2048 columns: 1.6 times as fast on the
-        // geometric mean, up to 3.4 (64 x 3072 x 768 with SwiGLU
-        // 17.2 -> 8.3 us, 128 x 8192 x 768 37 -> 18 us).
+        // Over a long contraction with a workspace: the 16-row tile (48, 96
+        // or 192 wide) and K split (none, two or four workgroups) of least
+        // estimated time (pick_by_estimate).  Not below 3072 for grids of
+        // more than half a round (splits there lost up to 18%), nor below
+        // 8192 for the eight-staging-wave SwiGLU tile (0.81 to 1.14 times as
+        // fast).  Against the choice above, over 16 to 768 rows,
+        // contractions of 2048 to 16384 and 512 to 2048 columns: 1.6 times
+        // as fast on the geometric mean, up to 3.4 (64 x 3072 x 768 with
+        // SwiGLU 17.2 -> 8.3 us, 128 x 8192 x 768 37 -> 18 us).
         const bool base48 = same_name(base, "16x48x128_k4_sp4_pf3_il_dA_wr2");
         const bool sp8 = same_name(base, "16x96x128_w1x2_k2_sp8_pf2_il_wr4");
         if (!split || K < (sp8 ? 8192 : 2048) || (K < 3072 && (base48 ? s48 : s96) > cus / 2)) return base;
-        struct Cand { int bn, ks; const char *name; };
-        static const Cand cands[] = {
-            {48, 1, "16x48x128_k4_sp4_pf3_il_dA_wr2"},         {96, 1, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"},
-            {48, 2, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"},     {96, 2, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"},
-            {192, 2, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"},    {48, 4, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"},
-            {96, 4, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"}, {192, 4, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"}};
-        auto cost = [&](int bn, int ks) {
-            const int64_t wgs = ceil_div(M, 16) * ceil_div(N, bn) * ks;
-            return (double)ceil_div(wgs, cus) * (double)ceil_div(K, ks) * (bn / 48.0 + (swiglu ? 0.5 : 0.0)) *
-                   (bn == 48 && wgs <= cus ? 1.2 : 1.0);
-        };
-        const char *best = base;
-        double best_cost = cost(base48 ? 48 : 96, 1);
-        for (const Cand &c : cands) {
-            const int64_t wgs = ceil_div(M, 16) * ceil_div(N, c.bn) * c.ks;
-            if (c.ks > 1 && (K / c.ks < (wgs > 2 * cus ? 1024 : 512) || c.ks * M * N > ((int64_t)1 << 20))) continue;
-            const double t = cost(c.bn, c.ks);
-            if (t < best_cost) best = c.name, best_cost = t;
-        }
-        return best;
+        static const SplitCand cands[] = {
+            {16, 48, 1, "16x48x128_k4_sp4_pf3_il_dA_wr2"},         {16, 96, 1, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"},
+            {16, 48, 2, "16x48x128_k4_sp4_pf3_il_ks2_dA_wr2"},     {16, 96, 2, "16x96x128_w1x2_k2_sp4_pf3_il_ks2_dA_wr4"},
+            {16, 192, 2, "16x192x128_w1x4_sp4_pf3_il_ks2_wr4"},    {16, 48, 4, "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"},
+            {16, 96, 4, "16x96x128_w1x2_k2_sp4_pf3_il_ks4_dA_wr4"}, {16, 192, 4, "16x192x128_w1x4_sp4_pf3_il_ks4_wr4"}};
+        return pick_by_estimate(M, K, N, swiglu, true, INT64_MAX, cands, sizeof(cands) / sizeof(cands[0]), base,
+                                split_estimate(M, K, N, swiglu, 16, base48 ? 48 : 96, 1));
     }
     // forward products: 128 x 48 where that grid fills the CUs, which stages
     // (and widens, or combines) each block of W (or A) half as often
@@ -1412,45 +1430,27 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     }
     if (!forward || !split || K < 2048) return small;
     // The forward products with binary16 W over a long contraction with a
-    // workspace: the tile and K split of least estimated time, as for fp32
-    // W above, with the work in units of 16 x 48 outputs (and the SwiGLU
-    // combine, done once per tile row, in half units per 16 rows).  Ties keep
-    // the choice above.  64 x 3072 x 768 with SwiGLU: 21.5 -> 9.7 us;
-    // 128 x 8192 x 768: 42.9 -> 20.2 us; 32 x 4096 x 1024: 22.4 -> 9.8 us.
-    // (SwiGLU takes the 32 x 96 two-way split in its W-only DMA form, as
-    // above)
-    const char *const split96 =
-        swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW";
-    struct Cand { int bm, bn, ks; const char *name; };
-    // (in this order, so that among equal estimates the first, with fewer
-    // and larger workgroups, is taken)
-    const Cand cands[] = {
+    // workspace: the tile and K split of least estimated time
+    // (pick_by_estimate; not below 3072 for grids of more than half a
+    // round), the 32-row tiles listed first so that equal estimates take
+    // fewer and larger workgroups.  SwiGLU takes the 32 x 96 two-way split
+    // in its W-only DMA form, as above.  64 x 3072 x 768 with SwiGLU:
+    // 21.5 -> 9.7 us; 128 x 8192 x 768: 42.9 -> 20.2 us; 32 x 4096 x 1024:
+    // 22.4 -> 9.8 us.
+    const SplitCand cands[] = {
         {32, 48, 1, "32x48x128_k4_sp8_pf2_dAW"},     {32, 48, 2, "32x48x128_k4_sp8_pf2_ks2_dAW"},
         {32, 48, 4, "32x48x128_k4_sp8_pf2_ks4_dAW"}, {16, 48, 1, "16x48x128_k4_sp4_dAW"},
         {16, 48, 2, "16x48x128_k4_sp4_ks2_dAW"},     {16, 48, 4, "16x48x128_k4_sp4_ks4_dAW"},
         {16, 96, 1, "16x96x128_w1x2_k2_sp8_pf3_il_cil_dW"},
-        {32, 96, 2, split96},
+        {32, 96, 2, swiglu ? "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dW" : "32x96x128_w1x2_k2_sp8_pf3_il_ks2_cil_dAW"},
         {32, 96, 4, "32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"}};
-    auto grid = [&](const Cand &c) { return ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.ks; };
-    auto cost = [&](const Cand &c) {
-        const int64_t wgs = grid(c);
-        return (double)ceil_div(wgs, cus) * (double)ceil_div(K, c.ks) *
-               (c.bm * c.bn / 768.0 + (swiglu ? c.bm / 32.0 : 0.0)) *
-               (c.bm == 16 && c.bn == 48 && wgs <= cus ? 1.2 : 1.0);
-    };
-    const Cand *base = nullptr;
-    for (const Cand &c : cands)
+    const int count = sizeof(cands) / sizeof(cands[0]);
+    const SplitCand *base = nullptr;
+    for (const SplitCand &c : cands)
         if (same_name(c.name, small)) base = &c;
-    if (base == nullptr || (K < 3072 && grid(*base) / base->ks > cus / 2)) return small;
-    const char *best = small;
-    double best_cost = cost(*base);
-    for (const Cand &c : cands) {
-        const int64_t wgs = grid(c);
-        if (c.ks > 1 && (K / c.ks < (wgs > 2 * cus ? 1024 : 512) || c.ks * M * N > ((int64_t)1 << 20))) continue;
-        const double t = cost(c);
-        if (t < best_cost) best = c.name, best_cost = t;
-    }
-    return best;
+    if (base == nullptr || (K < 3072 && ceil_div(M, base->bm) * ceil_div(N, base->bn) > cus / 2)) return small;
+    return pick_by_estimate(M, K, N, swiglu, true, INT64_MAX, cands, count, small,
+                            split_estimate(M, K, N, swiglu, base->bm, base->bn, base->ks));
 }
 
 // The forward choice: an index into kConfigs (-1 if the rule names a tile
@@ -1576,29 +1576,15 @@ int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool 
     for (const char *t : small_tiles) small = small || same_name(e.name, t);
     if (!small) return r;
     const int64_t cus = 256;
-    auto cost = [&](int bm, int bn, int ks) {
-        const int64_t wgs = ceil_div(M, bm) * ceil_div(N, bn) * ks;
-        return (double)ceil_div(wgs, cus) * (double)ceil_div(K, ks) * (bm * bn / 768.0) *
-               (bm == 16 && bn == 48 && wgs <= cus ? 1.2 : 1.0);
-    };
     const bool splits = split && K >= (ceil_div(M, 16) * ceil_div(N, 48) > cus / 2 ? 8192 : 2048);
-    struct Cand { int bm, bn, ks; const char *name; };
-    static const Cand cands[] = {
+    static const SplitCand cands[] = {
         {32, 48, 1, "32x48x128_k4_sp8_pf2_dAW"},     {32, 48, 2, "32x48x128_k4_sp8_pf2_ks2_dAW"},
         {32, 48, 4, "32x48x128_k4_sp8_pf2_ks4_dAW"}, {32, 48, 8, "32x48x128_k4_sp8_pf2_ks8_dAW"},
         {16, 48, 1, "16x48x128_k4_sp4_dAW"},         {16, 48, 2, "16x48x128_k4_sp4_ks2_dAW"},
         {16, 48, 4, "16x48x128_k4_sp4_ks4_dAW"},     {16, 48, 8, "16x48x128_k4_sp4_ks8_dAW"}};
-    int best = r;
-    double best_cost = deep ? 1e300 : cost(e.bm, e.bn, e.ks);
-    for (const Cand &c : cands) {
-        const int64_t wgs = ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.ks;
-        if (c.ks > 1 && (!splits || K / c.ks < (wgs > 2 * cus ? 1024 : 512) || wgs > 6 * cus ||
-                         c.ks * M * N > ((int64_t)1 << 20)))
-            continue;
-        const double t = cost(c.bm, c.bn, c.ks);
-        if (t < best_cost) best = table_index(kBwdConfigs, kNumBwdConfigs, c.name), best_cost = t;
-    }
-    return best;
+    const char *best = pick_by_estimate(M, K, N, false, splits, 6 * cus, cands, sizeof(cands) / sizeof(cands[0]),
+                                        e.name, deep ? -1.0 : split_estimate(M, K, N, false, e.bm, e.bn, e.ks));
+    return table_index(kBwdConfigs, kNumBwdConfigs, best);
 }
 
 // ---------------------------------------------------------------------------
