@@ -30,6 +30,62 @@ def test_ragged_shapes(M, N, K):
     check(c, run(c).cpu().numpy(), label="swiglu_w16")
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 4100, 4), (3, 2052, 4), (1, 8192, 48)])
+def test_split_k_on_tiny_outputs(M, K, N):
+    # one to three output rows over a long contraction: the library's
+    # choice splits K (every form below but SwiGLU with fp32 W at these
+    # lengths); each product with and without a workspace, every element
+    # against the oracle
+    import torch
+    b = _lib()
+    for sw, w16 in ((False, False), (True, False), (False, True), (True, True)):
+        tile = b.kernel_config(M, K, N, swiglu=sw, w16=w16)
+        say(f"tiny output {M}x{K}x{N} swiglu={sw} w16={w16} -> {tile}")
+        assert "_ks" in tile or (sw and not w16)
+        c = inputs.random_case(M + K + N + 2 * sw + w16, M, K, N, swiglu=sw, w16=w16, residual=sw, gate_scale=3.0)
+        d = {k: to_dev(v) for k, v in c.items()}
+        for ws in (True, False):
+            if sw:
+                y = b.matmul_residual_swiglu_a(d["G"], d["U"], d["W"], d["R"], use_workspace=ws)
+            else:
+                y = b.matmul(d["X"], d["W"], use_workspace=ws)
+            torch.cuda.synchronize()
+            check(c, y.cpu().numpy(), label=f"workspace={ws}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4, 4100), (3, 8, 8196)])
+def test_split_k_on_tiny_backward_outputs(M, K, N):
+    # the backward products onto one to three rows (dX) or a 4 x 4 / 8 x 4
+    # block (dW) over a long contraction: K split with a workspace, not
+    # without; every element against the oracle
+    import torch
+    b = _lib()
+    assert "_ks" in b.bwd_kernel_config("matmul_t", M, K, N)
+    c = inputs.backward_case(M + K + N, M, K, N)
+    for ws in (True, False):
+        y = b.matmul_t(to_dev(c["dY"]), to_dev(c["W"]), use_workspace=ws)
+        torch.cuda.synchronize()
+        ref, scale = oracle.matmul_t(c["dY"], c["W"], want_scale=True)
+        res = oracle.compare(y.cpu().numpy(), ref, scale, oracle.TOL_W32)
+        say(f"  matmul_t {M}x{K}x{N} workspace={ws}: max err/tol {res['max_ratio']:.3g}")
+        assert res["fails"] == 0, res
+    # dW [K2 x N2] over N tokens
+    T, K2, N2 = N, K, 4
+    assert "_ks" in b.bwd_kernel_config("matmul_at", T, K2, N2)
+    c = inputs.backward_case(T + K2, T, K2, N2, swiglu=True, gate_scale=3.0)
+    for sw in (False, True):
+        for ws in (True, False):
+            if sw:
+                y = b.matmul_at_swiglu_a(to_dev(c["G"]), to_dev(c["U"]), to_dev(c["dY"]), use_workspace=ws)
+            else:
+                y = b.matmul_at(to_dev(c["G"]), to_dev(c["dY"]), use_workspace=ws)
+            torch.cuda.synchronize()
+            ref, scale = oracle.matmul_at(c["G"], c["dY"], U=c["U"] if sw else None, want_scale=True)
+            res = oracle.compare(y.cpu().numpy(), ref, scale, oracle.TOL_W32)
+            say(f"  matmul_at{'_swiglu_a' if sw else ''} {T}x{K2}x{N2} workspace={ws}: max err/tol {res['max_ratio']:.3g}")
+            assert res["fails"] == 0, res
+
+
 def test_k_zero():
     import torch
     b = _lib()
