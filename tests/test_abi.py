@@ -113,6 +113,13 @@ def test_config_table(lib):
     assert pick(128, 8192, 768, 0, 1) == "32x48x128_k4_sp8_pf2_ks4_dAW"
     assert pick(256, 3072, 768, 1, 1) == "32x96x128_w1x2_k2_sp8_pf3_il_ks4_cil_dAW"
     assert pick(128, 8192, 768, 0, 1, ws=0) == "16x48x128_k4_sp4_dAW"
+    # few rows against a wide W: 16-row tiles instead of 128 x 64 / 64 x 64
+    assert pick(16, 768, 50304, 0, 1) == "16x48x128_k4_sp4_dAW"
+    assert pick(16, 768, 16384, 0, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert pick(48, 768, 50304, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(48, 4096, 16384, 0, 0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(64, 768, 50304, 0, 1) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(65, 768, 50304, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
     # below 3072 of contraction only grids of at most half a round split
     assert pick(64, 2048, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
     assert pick(128, 2048, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"

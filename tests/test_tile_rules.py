@@ -37,6 +37,13 @@ def _rows(M, seed, count=48, tail=128):
     (2048, 768, 768, False, False, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (2040, 768, 760, False, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (512, 2000, 768, False, False, "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"),
+    # few rows against a wide W: no 128-row tiles at 64 rows or fewer, no
+    # 64-row tiles at 32 or fewer (48 with fp32 W beyond one round)
+    (16, 768, 50304, True, False, "16x48x128_k4_sp4_dAW"),
+    (1, 768, 50304, False, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (48, 768, 50304, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (17, 768, 16388, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (64, 768, 50304, True, False, "64x64x64_w2x2_sp4_dAW"),
 ])
 def test_forward_rule(M, K, N, w16, resid, tile):
     from tiled_dense_gemm_matmul_amd import binding

@@ -1363,15 +1363,28 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     if (wide_swiglu && forward && !w16)
         return ceil_div(N, 384) * 384 * 10 <= N * 11 ? "32x384x64_w1x4_sp4_pf3_il_dA_wr2"
                                                       : "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
-    if (ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
-    if (wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
+    // Forward products with few rows (decoding a few tokens against a wide
+    // W): no 128-row tiles for 64 rows or fewer, no 64-row tiles for 32 or
+    // fewer, however many columns, as most of such a tile's MFMA work would
+    // be padding; with fp32 W, whose 16-row tiles hold W in registers, no
+    // 64-row tiles over more than one round for 48 or fewer either (the one
+    // whole round of 64 x 64 tiles below stays).  16 x 768 x 50304 with
+    // binary16 W: 23.1 against 95.2 us on 128 x 64; 16 x 768 x 16384: 9.4
+    // against 16.4 on 64 x 64; 48 x 768 x 50304 with fp32 W: 37.8 against
+    // 95.2 (128 x 64) and 50.9 (64 x 64); 64 x 4096 x 50304 with binary16 W:
+    // 259 against 489 us on 128 x 64.
+    const bool rows128 = !forward || M > 64, rows64 = !forward || M > (w16 ? 32 : 48);
+    const bool rows64_round = !forward || M > 32;
+    if (rows128 && ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
+    if (rows64 && wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
-    if (forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return "128x64x32_w2x2_sp4_pf3_il_dA";
-    if (ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
+    if (rows128 && forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return "128x64x32_w2x2_sp4_pf3_il_dA";
+    if (rows128 && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
-    if (t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
-    if (forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) return "64x64x64_w2x2_sp4_dAW";
+    if (rows64 && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
+    if (rows64_round && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus)
+        return "64x64x64_w2x2_sp4_dAW";
     // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
     if (forward && !w16) {
@@ -1412,8 +1425,8 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     }
     // forward products: 128 x 48 where that grid fills the CUs, which stages
     // (and widens, or combines) each block of W (or A) half as often
-    if (forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
-    if (t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
+    if (rows128 && forward && ceil_div(M, 128) * ceil_div(N, 48) >= cus) return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
+    if (rows64 && t48 >= cus) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
     const char *small = nullptr;
     if (M <= 128) small = "16x48x128_k4_sp4_dAW";
     else if (K >= 2048) {
