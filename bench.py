@@ -268,8 +268,11 @@ def time_loss():
         total = torch.empty(1, device=dev)
         sl_us = batch_time(lambda: lib.loss_sum_losses(losses.data_ptr(), total.data_ptr(), S, st.cuda_stream), 20)
         nbytes = 2 * S * V * 4 + 2 * S * 4
-        path = "registers, 256 threads/row" if V <= 16384 else ("registers, 1024 threads/row" if V <= 65536
-                                                                 else "streaming")
+        # the library's launch shape for rows of V logits (16-byte accesses)
+        shape = next(((nt, cap) for nt, cap, lim in ((256, 16, 4096), (512, 16, 8192), (512, 32, 16384),
+                                                      (1024, 32, 32768), (1024, 64, 65536)) if V <= lim), None)
+        path = f"registers, {shape[0]} threads x {shape[1]} logits/row" if shape and V % 4 == 0 else \
+            ("registers, 256 threads x 64 logits/row" if V <= 16384 else "streaming")
         row = {"S": S, "V": V, "warm_us": round(warm, 2), "warm_GBps": round(nbytes / warm / 1e3, 1),
                "cold_us": round(cold, 2), "cold_GBps": round(nbytes / cold / 1e3, 1),
                "frac_hbm_peak_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4), "sum_losses_us": round(sl_us, 2)}

@@ -145,7 +145,7 @@ def test_fused_swiglu_backward_every_config(cfg):
     check_fused(du.result(name), ru, bu, f"dUP {name}")
 
 
-@pytest.mark.parametrize("S,V", [(37, 1003), (33, 4096), (5, 70001)])
+@pytest.mark.parametrize("S,V", [(37, 1003), (33, 4096), (11, 8196), (7, 20000), (5, 70001)])
 def test_loss_kernels(S, V):
     """cross_entropy rewrites the logits in place: they sit inside sentinel
     bands that must neither be read (the losses would change) nor written;

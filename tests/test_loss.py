@@ -53,7 +53,11 @@ def test_seq512_full(alpha, beta):
 
 
 @pytest.mark.parametrize("S,V", [(40, 1001), (9, 3), (5, 1), (12, 20001), (6, 70000), (16, 65536), (33, 50304),
-                                 (7, 16388)])
+                                 (7, 16388),
+                                 # each row length's launch shape and its edges:
+                                 # 256 x 16, 512 x 16, 512 x 32, 1024 x 32, 1024 x 64
+                                 (24, 1000), (19, 4096), (19, 4100), (13, 8192), (13, 8196), (11, 12288),
+                                 (9, 32000), (10, 32768), (10, 32772)])
 def test_paths_and_ragged_vocab(S, V):
     say(f"cross_entropy S={S} V={V}")
     case = inputs.loss_case(S * 31 + V, S, V, scale=3.0, ignore_every=5)
