@@ -120,6 +120,11 @@ def test_config_table(lib):
     assert pick(48, 4096, 16384, 0, 0) == "64x64x64_w2x2_sp4_dAW"
     assert pick(64, 768, 50304, 0, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(65, 768, 50304, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    # few columns: no tile more than twice as wide as the columns it covers
+    assert pick(8192, 768, 48, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
+    assert pick(32768, 768, 64, 0, 0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(32768, 768, 64, 1, 0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(8192, 3072, 32, 1, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     # below 3072 of contraction only grids of at most half a round split
     assert pick(64, 2048, 768, 0, 0) == "16x48x128_k4_sp4_pf3_il_ks4_dA_wr2"
     assert pick(128, 2048, 1024, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"

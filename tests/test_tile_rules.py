@@ -44,6 +44,10 @@ def _rows(M, seed, count=48, tail=128):
     (48, 768, 50304, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (17, 768, 16388, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (64, 768, 50304, True, False, "64x64x64_w2x2_sp4_dAW"),
+    # few columns: no tile more than twice as wide as the columns it covers
+    (8192, 768, 48, False, False, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (32768, 768, 64, False, True, "64x64x64_w2x2_sp4_dAW"),
+    (8191, 772, 64, True, True, "64x48x64_w2x1_k2_sp4_pf3_il_dA"),
 ])
 def test_forward_rule(M, K, N, w16, resid, tile):
     from tiled_dense_gemm_matmul_amd import binding
@@ -64,6 +68,8 @@ def test_forward_rule(M, K, N, w16, resid, tile):
     (8192, 1024, 768, True, "32x384x64_w1x4_sp4_pf3_il_dA_wr2"),
     (8191, 1024, 772, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (384, 2048, 768, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
+    (8192, 3072, 32, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
+    (8190, 3076, 36, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
 ])
 def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):
     import torch

@@ -1355,12 +1355,18 @@ const char *pick_by_estimate(int64_t M, int64_t K, int64_t N, bool swiglu, bool 
 // backward table.
 const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward) {
     const int64_t cus = 256;
+    // Forward products with few columns (a narrow W): no tile more than
+    // twice as wide as the columns it covers, since most of its MFMA work
+    // would be padding (8192 x 768 x 48 with fp32 W: 7.0 against 20.1 us on
+    // 32 x 192; 32768 x 768 x 64: 27.7 on 64 x 64 against 72.8 on
+    // 128 x 192).
+    auto cols = [&](int bn) { return !forward || N * 2 > ceil_div(N, bn) * bn; };
     const bool wide_swiglu = swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus;
     // SwiGLU with fp32 W on a large grid (ahead of 128 x 128, which combines
     // each element of A once per 128 columns): 32 x 384 tiles with W in
     // registers, or 32 x 192 where 384-wide tiles would leave more than a
     // tenth of their columns past N
-    if (wide_swiglu && forward && !w16)
+    if (wide_swiglu && forward && !w16 && cols(192))
         return ceil_div(N, 384) * 384 * 10 <= N * 11 ? "32x384x64_w1x4_sp4_pf3_il_dA_wr2"
                                                       : "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
     // Forward products with few rows (decoding a few tokens against a wide
@@ -1375,15 +1381,16 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     // 259 against 489 us on 128 x 64.
     const bool rows128 = !forward || M > 64, rows64 = !forward || M > (w16 ? 32 : 48);
     const bool rows64_round = !forward || M > 32;
-    if (rows128 && ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
-    if (rows64 && wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
+    if (rows128 && cols(128) && ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
+    if (rows64 && cols(384) && wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
-    if (rows128 && forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus) return "128x64x32_w2x2_sp4_pf3_il_dA";
-    if (rows128 && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
+    if (rows128 && cols(64) && forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus)
+        return "128x64x32_w2x2_sp4_pf3_il_dA";
+    if (rows128 && cols(192) && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
-    if (rows64 && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
-    if (rows64_round && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus)
+    if (rows64 && cols(64) && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
+    if (rows64_round && cols(64) && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus)
         return "64x64x64_w2x2_sp4_dAW";
     // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
@@ -1391,13 +1398,18 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
         // every smaller grid with fp32 W: tiles with W in registers; 32 x 192
         // where that grid fills whole rounds of the CUs (nine tenths or more)
         const int64_t t32w = ceil_div(M, 32) * ceil_div(N, 192);
-        if (t32w >= cus && fill(t32w) >= 0.9) return "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
-        if (swiglu && K >= 2048 && split && M * N <= kSplitMaxElems && ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
+        if (cols(192) && t32w >= cus && fill(t32w) >= 0.9) return "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
+        if (swiglu && cols(192) && K >= 2048 && split && M * N <= kSplitMaxElems &&
+            ceil_div(M, 16) * ceil_div(N, 192) * 2 >= cus)
             return "16x192x128_w1x4_sp4_pf3_il_ks2_wr4";
-        // 16 x 48 where its grid fills whole rounds better (with SwiGLU,
-        // which it combines twice as often, only below one round of 16 x 96)
+        // 16 x 48 where its grid fills whole rounds better, counting only
+        // the columns each tile covers (with SwiGLU, which it then combines
+        // more often, only below one round of 16 x 96)
         const int64_t s96 = ceil_div(M, 16) * ceil_div(N, 96), s48 = ceil_div(M, 16) * ceil_div(N, 48);
-        const char *base = fill(s96) < fill(s48) && (!swiglu || s96 < cus) ? "16x48x128_k4_sp4_pf3_il_dA_wr2"
+        const double u96 = (double)N / (double)(ceil_div(N, 96) * 96), u48 = (double)N / (double)(ceil_div(N, 48) * 48);
+        const bool more48 = ceil_div(N, 48) > ceil_div(N, 96);
+        const char *base = fill(s96) * u96 < fill(s48) * u48 && (!swiglu || !more48 || s96 < cus)
+                               ? "16x48x128_k4_sp4_pf3_il_dA_wr2"
                            // SwiGLU on one round at most: eight staging
                            // waves; otherwise four, which lets two
                            // workgroups share a CU
