@@ -391,6 +391,10 @@ def test_backward_selection(lib):
     assert name(2, 16384, 768, 768) == "48x48x64_k4_sp4_pf2_ks2_dAW"
     assert name(2, 2048, 768, 768) == "48x48x64_k4_sp4_pf2_ks2_dAW"
     assert name(2, 8192, 768, 768, ws=0) == "48x48x64_k4_sp4_pf3_dAW"
+    # a narrow dX over many tokens: no tile more than twice as wide as its
+    # columns
+    assert name(1, 32768, 64, 768) == "64x64x64_w2x2_sp4"
+    assert name(1, 32768, 16, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(2, 1024, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
     assert name(2, 1024, 512, 512) == "48x48x64_k4_sp4_pf2_ks2_dAW"
     assert name(2, 2048, 512, 512) == "48x48x64_k4_sp4_pf2_ks4_dAW"

@@ -164,6 +164,22 @@ def test_backward_matmul_t_split_small_outputs(M, K, N, tile):
     check_fused(du.cpu().numpy(), ru, bu, "dUP")
 
 
+@pytest.mark.parametrize("M,K,N,tile", [(32768, 64, 768, "64x64x64_w2x2_sp4"),
+                                        (32767, 20, 772, "64x48x64_w2x1_k2_sp4_pf3_il_dA")])
+def test_backward_matmul_t_narrow_output(M, K, N, tile):
+    # dX = dY @ W^T onto a narrow dX (a layer with few inputs) over many
+    # tokens: no tile more than twice as wide as the columns it covers
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.bwd_kernel_config("matmul_t", M, K, N) == tile
+    c = inputs.backward_case(21 + K, M, K, N)
+    dX = binding.matmul_t(to_dev(c["dY"]), to_dev(c["W"]))
+    torch.cuda.synchronize()
+    rows = _rows(M, 12)
+    ref, scale = oracle.matmul_t(c["dY"], c["W"], rows=rows, want_scale=True)
+    _cmp(dX.cpu().numpy()[rows], ref, scale, f"matmul_t {M}x{K}x{N} {tile}")
+
+
 def test_backward_matmul_t_128x64():
     # dX = dY @ W^T for 8192 tokens, 768 outputs, 768 inputs
     import torch

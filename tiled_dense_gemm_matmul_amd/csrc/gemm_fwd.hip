@@ -1355,12 +1355,13 @@ const char *pick_by_estimate(int64_t M, int64_t K, int64_t N, bool swiglu, bool 
 // backward table.
 const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bool split, bool forward) {
     const int64_t cus = 256;
-    // Forward products with few columns (a narrow W): no tile more than
-    // twice as wide as the columns it covers, since most of its MFMA work
-    // would be padding (8192 x 768 x 48 with fp32 W: 7.0 against 20.1 us on
-    // 32 x 192; 32768 x 768 x 64: 27.7 on 64 x 64 against 72.8 on
-    // 128 x 192).
-    auto cols = [&](int bn) { return !forward || N * 2 > ceil_div(N, bn) * bn; };
+    // Products with few columns (a narrow W, or the input gradient of a
+    // narrow layer): no tile more than twice as wide as the columns it
+    // covers, since most of its MFMA work would be padding (8192 x 768 x 48
+    // with fp32 W: 7.0 against 20.1 us on 32 x 192; 32768 x 768 x 64: 27.7
+    // on 64 x 64 against 72.8 on 128 x 192; matmul_t onto 32768 x 64: 30.6
+    // on 64 x 64 against 78.0 on 128 x 192).
+    auto cols = [&](int bn) { return N * 2 > ceil_div(N, bn) * bn; };
     const bool wide_swiglu = swiglu && ceil_div(M, 64) * ceil_div(N, 384) >= cus;
     // SwiGLU with fp32 W on a large grid (ahead of 128 x 128, which combines
     // each element of A once per 128 columns): 32 x 384 tiles with W in
