@@ -117,9 +117,18 @@ def test_config_table(lib):
     assert pick(16, 768, 50304, 0, 1) == "16x48x128_k4_sp4_dAW"
     assert pick(16, 768, 16384, 0, 0) == "16x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert pick(48, 768, 50304, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
-    assert pick(48, 4096, 16384, 0, 0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(48, 4096, 16384, 0, 0) == "64x64x64_w2x2_sp4_ks2_dAW"
+    assert pick(48, 4096, 16384, 0, 0, ws=0) == "64x64x64_w2x2_sp4_dAW"
     assert pick(64, 768, 50304, 0, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(65, 768, 50304, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    # one whole round of 64 x 64 tiles over a long contraction: K split in two
+    # with a workspace (SwiGLU only while the split fits the library-held
+    # scratch)
+    assert pick(1024, 4096, 1024, 0, 0) == "64x64x64_w2x2_sp4_ks2_dAW"
+    assert pick(1024, 4096, 1024, 0, 1) == "64x64x64_w2x2_sp4_ks2_dAW"
+    assert pick(1024, 4096, 1024, 0, 0, ws=0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(1024, 1024, 1024, 0, 0) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(1024, 4096, 1024, 1, 0) == "64x64x64_w2x2_sp4_dAW"
     # few columns: no tile more than twice as wide as the columns it covers
     assert pick(8192, 768, 48, 0, 0) == "16x48x128_k4_sp4_pf3_il_dA_wr2"
     assert pick(32768, 768, 64, 0, 0) == "64x64x64_w2x2_sp4_dAW"

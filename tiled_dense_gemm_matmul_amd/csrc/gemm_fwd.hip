@@ -1121,6 +1121,9 @@ const ConfigEntry kConfigs[] = {
     make_entry<Tile<128, 192, 32, 2, 2, 1, 8, 4, 1, 1>>("128x192x32_w2x2_sp8_pf4_il"),
     make_entry<Tile<128, 64, 32, 2, 2, 1, 4, 3, 1, 1, 1, 0, 2, 1>>("128x64x32_w2x2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 1, 0, 2, 3>>("64x64x64_w2x2_sp4_dAW"),
+    // the same tile with K split over two workgroups (one whole round of
+    // tiles over a long contraction)
+    make_entry<Tile<64, 64, 64, 2, 2, 1, 4, 2, 1, 0, 2, 0, 2, 3>>("64x64x64_w2x2_sp4_ks2_dAW"),
     make_entry<Tile<128, 48, 32, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("128x48x32_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<64, 48, 64, 2, 1, 2, 4, 3, 1, 1, 1, 0, 2, 1>>("64x48x64_w2x1_k2_sp4_pf3_il_dA"),
     make_entry<Tile<32, 48, 128, 1, 1, 4, 8, 2, 1, 0, 1, 0, 2, 3>>("32x48x128_k4_sp8_pf2_dAW"),
@@ -1391,8 +1394,16 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     if (rows128 && cols(192) && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
     if (rows64 && cols(64) && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
-    if (rows64_round && cols(64) && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus)
+    if (rows64_round && cols(64) && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) {
+        // over a contraction of 2048 or more with a workspace, K split in
+        // two: two workgroups per CU instead of one (1024 x 4096 x 1024:
+        // 67.2 against 71.8 us with fp32 W, 70.9 against 77.3 with binary16
+        // W; 1024 x 8192 x 1024: 129.6 against 141.0; at a contraction of
+        // 1024 the split lost, 21.3 against 20.2); with SwiGLU only while
+        // the partial tiles fit the allocation-free entry point's scratch
+        if (split && K >= 2048 && (!swiglu || 2 * M * N <= ((int64_t)1 << 20))) return "64x64x64_w2x2_sp4_ks2_dAW";
         return "64x64x64_w2x2_sp4_dAW";
+    }
     // the fraction of whole rounds of the CUs a grid of t tiles keeps busy
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
     if (forward && !w16) {
