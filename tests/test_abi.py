@@ -403,6 +403,11 @@ def test_backward_selection(lib):
     # a narrow dX over many tokens: no tile more than twice as wide as its
     # columns
     assert name(1, 32768, 64, 768) == "64x64x64_w2x2_sp4"
+    # a transposed B where the rule takes 64 x 64: 64 x 48 where 48-wide
+    # tiles cover the columns at least as fully
+    assert name(1, 16384, 96, 3072) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert name(1, 4096, 768, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert name(1, 8192, 256, 768) == "64x64x64_w2x2_sp4"
     assert name(1, 32768, 16, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(2, 1024, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"
     assert name(2, 1024, 512, 512) == "48x48x64_k4_sp4_pf2_ks2_dAW"

@@ -168,7 +168,8 @@ def test_backward_matmul_t_split_small_outputs(M, K, N, tile):
 
 
 @pytest.mark.parametrize("M,K,N,tile", [(32768, 64, 768, "64x64x64_w2x2_sp4"),
-                                        (32767, 20, 772, "64x48x64_w2x1_k2_sp4_pf3_il_dA")])
+                                        (32767, 20, 772, "64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+                                        (16383, 96, 3076, "64x48x64_w2x1_k2_sp4_pf3_il_dA")])
 def test_backward_matmul_t_narrow_output(M, K, N, tile):
     # dX = dY @ W^T onto a narrow dX (a layer with few inputs) over many
     # tokens: no tile more than twice as wide as the columns it covers

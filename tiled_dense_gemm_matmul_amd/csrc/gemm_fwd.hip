@@ -1572,6 +1572,13 @@ int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool sp
     // a transposed A takes 32 x 48 tiles where the rule takes 64 x 64
     // (whose backward form stages with registers)
     const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
+    // a transposed B where the rule takes 64 x 64: 64 x 48 tiles whenever
+    // 48-wide tiles cover the columns at least as fully (dX onto 96 columns
+    // over 16384 tokens, contraction 3072: 77.6 against 102.4 us; onto 192
+    // and 384 columns 4-5% faster; onto 256, where 48-wide tiles leave a
+    // ninth of their columns past N, 64 x 64 stays, 7% faster)
+    if (op == kOpNT && same_name(r, mid) && N * 64 * ceil_div(N, 64) >= N * 48 * ceil_div(N, 48))
+        return bwd("64x48x64_w2x1_k2_sp4_pf3_il_dA");
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
     const bool tn_small = op == kOpTN && (same_name(r, small) || same_name(f, deep));
     // a transposed B on the smallest grids: 128-deep slices, eight staging
