@@ -223,6 +223,21 @@ def test_backward_matmul_at_48x48_long_contraction(M, K, N, ks):
     _cmp(out.cpu().numpy()[rows], ref, scale, f"matmul_at_acc {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(1024, 3072, 3072), (1023, 3076, 3068)])
+def test_backward_matmul_at_w_in_registers_partial_round(M, K, N):
+    # dW over 1024 tokens onto 3072 x 3072, where 128 x 128 tiles would fill
+    # under 70% of their rounds: dY in registers
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.bwd_kernel_config("matmul_at", M, K, N) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    c = inputs.backward_case(31 + N, M, K, N)
+    dW = binding.matmul_at(to_dev(c["X"]), to_dev(c["dY"]))
+    torch.cuda.synchronize()
+    rows = _rows(K, 13, count=64, tail=96)
+    ref, scale = oracle.matmul_at(c["X"], c["dY"], rows=rows, want_scale=True)
+    _cmp(dW.cpu().numpy()[rows], ref, scale, f"matmul_at {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("tokens", [512, 8192])
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_backward_matmul_at_w_in_registers(swiglu, tokens):

@@ -1571,6 +1571,18 @@ int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool sp
     }
     // a transposed A takes 32 x 48 tiles where the rule takes 64 x 64
     // (whose backward form stages with registers)
+    // a transposed A where the rule's 128 x 128 grid spans more than one
+    // round of two workgroups per CU but fills under 70% of the rounds it
+    // takes: the 32 x 96 tiles with dY in registers, where their own grid
+    // fills three quarters of its rounds or more (3072 x 1024 x 3072: 151.7
+    // against 188.5 us; 3072 x 2048 x 3072: 291 against 372; where
+    // 128 x 128 fills its rounds, as at 4096 x 1024 x 4096, it stays)
+    if (op == kOpTN && same_name(f, "128x128x32_w2x2_sp4_pf3_il_dA")) {
+        const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t96 = ceil_div(M, 32) * ceil_div(N, 96);
+        const double fill128 = (double)t128 / (double)(ceil_div(t128, 2 * cus) * 2 * cus);
+        const double fill96 = (double)t96 / (double)(ceil_div(t96, cus) * cus);
+        if (t128 > 2 * cus && fill128 < 0.7 && fill96 >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
+    }
     const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
     // a transposed B where the rule takes 64 x 64: 64 x 48 tiles whenever
     // 48-wide tiles cover the columns at least as fully (dX onto 96 columns
