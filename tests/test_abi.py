@@ -121,6 +121,9 @@ def test_config_table(lib):
     assert pick(48, 4096, 16384, 0, 0, ws=0) == "64x64x64_w2x2_sp4_dAW"
     assert pick(64, 768, 50304, 0, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(65, 768, 50304, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    # 128 x 128 only where its grid fills 70% of its rounds
+    assert pick(3072, 768, 3072, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert pick(4096, 768, 4096, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # one whole round of 64 x 64 tiles over a long contraction: K split in two
     # with a workspace (SwiGLU only while the split fits the library-held
     # scratch)

@@ -44,6 +44,9 @@ def _rows(M, seed, count=48, tail=128):
     (48, 768, 50304, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (17, 768, 16388, False, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (64, 768, 50304, True, False, "64x64x64_w2x2_sp4_dAW"),
+    # a 128 x 128 grid that fills under 70% of its rounds (576 tiles)
+    (3072, 768, 3072, True, False, "128x64x32_w2x2_sp4_pf3_il_dA"),
+    (3070, 772, 3068, True, True, "128x64x32_w2x2_sp4_pf3_il_dA"),
     # one whole round of 64 x 64 tiles over a long contraction: K split in two
     (1024, 4096, 1024, False, False, "64x64x64_w2x2_sp4_ks2_dAW"),
     (1000, 4100, 1020, True, True, "64x64x64_w2x2_sp4_ks2_dAW"),

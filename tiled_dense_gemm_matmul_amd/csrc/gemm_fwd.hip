@@ -1385,7 +1385,13 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     // 259 against 489 us on 128 x 64.
     const bool rows128 = !forward || M > 64, rows64 = !forward || M > (w16 ? 32 : 48);
     const bool rows64_round = !forward || M > 32;
-    if (rows128 && cols(128) && ceil_div(M, 128) * ceil_div(N, 128) >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
+    // forward products: 128 x 128 only where its grid fills 70% or more of
+    // the rounds of two workgroups per CU it takes (576 tiles, 3072 x K x
+    // 3072, take 1.125 rounds: 138 against 118 us on 128 x 64 with binary16
+    // W at 3072 x 768 x 3072, 109 on 32 x 192 with fp32 W)
+    const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+    const bool fill128 = !forward || t128 * 10 >= ceil_div(t128, 2 * cus) * 2 * cus * 7;
+    if (rows128 && cols(128) && fill128 && t128 >= 2 * cus) return "128x128x32_w2x2_sp4_pf3_il_dA";
     if (rows64 && cols(384) && wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
