@@ -411,6 +411,11 @@ def test_backward_selection(lib):
     assert name(1, 16384, 96, 3072) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(1, 4096, 768, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(1, 8192, 256, 768) == "64x64x64_w2x2_sp4"
+    # dX whose 128 x 128 grid spans more than one round of two per CU but
+    # fills under 70% of its rounds: 128 x 64
+    assert name(1, 3072, 3072, 768) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert name(1, 1536, 6144, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    assert name(1, 4096, 4096, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # dW whose 128 x 128 grid fills under 70% of its rounds: dY in registers
     assert name(2, 1024, 3072, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(2, 1024, 4096, 4096) == "128x128x32_w2x2_sp4_pf3_il_dA"

@@ -187,6 +187,21 @@ def test_backward_matmul_t_narrow_output(M, K, N, tile):
     _cmp(dX.cpu().numpy()[rows], ref, scale, f"matmul_t {M}x{K}x{N} {tile}")
 
 
+@pytest.mark.parametrize("M,K,N", [(3072, 3072, 768), (3001, 3052, 772)])
+def test_backward_matmul_t_partial_round(M, K, N):
+    # dX = dY @ W^T onto 3072 x 3072 (and a ragged neighbour), where 128 x 128
+    # tiles would fill under 70% of their rounds: 128 x 64
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.bwd_kernel_config("matmul_t", M, K, N) == "128x64x32_w2x2_sp4_pf3_il_dA"
+    c = inputs.backward_case(41 + K, M, K, N)
+    dX = binding.matmul_t(to_dev(c["dY"]), to_dev(c["W"]))
+    torch.cuda.synchronize()
+    rows = _rows(M, 17)
+    ref, scale = oracle.matmul_t(c["dY"], c["W"], rows=rows, want_scale=True)
+    _cmp(dX.cpu().numpy()[rows], ref, scale, f"matmul_t {M}x{K}x{N}")
+
+
 def test_backward_matmul_t_128x64():
     # dX = dY @ W^T for 8192 tokens, 768 outputs, 768 inputs
     import torch

@@ -1589,6 +1589,15 @@ int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool sp
         const double fill96 = (double)t96 / (double)(ceil_div(t96, cus) * cus);
         if (t128 > 2 * cus && fill128 < 0.7 && fill96 >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
     }
+    // a transposed B where the rule's 128 x 128 grid spans more than one
+    // round of two workgroups per CU but fills under 70% of the rounds it
+    // takes: 128 x 64 tiles (dX onto 3072 x 3072, contraction 768: 118.5
+    // against 142 us; contraction 3072: 456 against 548)
+    if (op == kOpNT && same_name(f, "128x128x32_w2x2_sp4_pf3_il_dA")) {
+        const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+        if (t128 > 2 * cus && t128 * 10 < ceil_div(t128, 2 * cus) * 2 * cus * 7)
+            return bwd("128x64x32_w2x2_sp4_pf3_il_dA");
+    }
     const char *r = same_name(f, fwd_mid) ? (op == kOpTN ? small : mid) : f;
     // a transposed B where the rule takes 64 x 64: 64 x 48 tiles whenever
     // 48-wide tiles cover the columns at least as fully (dX onto 96 columns
