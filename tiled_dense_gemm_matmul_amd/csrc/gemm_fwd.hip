@@ -1395,8 +1395,22 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     if (rows64 && cols(384) && wide_swiglu) return "64x384x32_w1x4_sp8_pf4_il";
     // forward products: 128 x 64 wherever that gives two tiles per CU, which
     // covers every grid 128 x 192 would fill; the backward rule keeps 128 x 192
-    if (rows128 && cols(64) && forward && ceil_div(M, 128) * ceil_div(N, 64) >= 2 * cus)
-        return "128x64x32_w2x2_sp4_pf3_il_dA";
+    const int64_t t128x64 = ceil_div(M, 128) * ceil_div(N, 64);
+    if (rows128 && cols(64) && forward && t128x64 >= 2 * cus) {
+        if (t128x64 * 10 >= ceil_div(t128x64, 2 * cus) * 2 * cus * 7) return "128x64x32_w2x2_sp4_pf3_il_dA";
+        // a 128 x 64 grid filling under 70% of its rounds of two per CU (576
+        // tiles at 3072 x 768 x 1536 took 72 us): fp32 W in registers on
+        // 32 x 192 tiles where their grid fills whole rounds (55), f16 W
+        // without SwiGLU on 128 x 48 tiles where theirs fills whole rounds of
+        // three per CU (58); otherwise on to the 64 x 64 tiles (68, and 83
+        // against 105 with SwiGLU), which without SwiGLU lost where the grid
+        // fills 60% or more (648 tiles at 2304 x 768 x 2304: 79 against 72)
+        const int64_t t32w = ceil_div(M, 32) * ceil_div(N, 192), t128x48 = ceil_div(M, 128) * ceil_div(N, 48);
+        if (!w16 && cols(192) && t32w * 10 >= ceil_div(t32w, cus) * cus * 9) return "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
+        if (w16 && !swiglu && t128x48 * 10 >= ceil_div(t128x48, 3 * cus) * 3 * cus * 9)
+            return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
+        if (!swiglu && t128x64 * 10 >= ceil_div(t128x64, 2 * cus) * 2 * cus * 6) return "128x64x32_w2x2_sp4_pf3_il_dA";
+    }
     if (rows128 && cols(192) && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
     if (rows64 && cols(64) && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
