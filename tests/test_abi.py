@@ -426,6 +426,11 @@ def test_backward_selection(lib):
     # dW whose 128 x 128 grid fills under 70% of its rounds: dY in registers
     assert name(2, 1024, 3072, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(2, 1024, 4096, 4096) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    # dW whose 128 x 192 grid spans more than one round: dY in registers; one
+    # whole round of 128 x 192 stays
+    assert name(2, 1024, 2304, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert name(2, 4096, 4608, 1792) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
+    assert name(2, 1024, 2048, 3072) == "128x192x32_w2x2_sp8_pf4_il"
     assert name(2, 512, 768, 16384) == "128x128x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 32768, 16, 768) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     assert name(2, 1024, 768, 768) == "48x48x64_k4_sp4_pf3_dAW"

@@ -249,10 +249,10 @@ def test_backward_matmul_at_48x48_long_contraction(M, K, N, ks):
     _cmp(out.cpu().numpy()[rows], ref, scale, f"matmul_at_acc {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(1024, 3072, 3072), (1023, 3076, 3068)])
+@pytest.mark.parametrize("M,K,N", [(1024, 3072, 3072), (1023, 3076, 3068), (1024, 2304, 3072), (1000, 2300, 3068)])
 def test_backward_matmul_at_w_in_registers_partial_round(M, K, N):
-    # dW over 1024 tokens onto 3072 x 3072, where 128 x 128 tiles would fill
-    # under 70% of their rounds: dY in registers
+    # dW over 1024 tokens onto 3072 x 3072 (and 2304 x 3072), where 128 x 128
+    # (128 x 192) tiles would fill under 70% of their rounds: dY in registers
     import torch
     from tiled_dense_gemm_matmul_amd import binding
     assert binding.bwd_kernel_config("matmul_at", M, K, N) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"

@@ -1410,6 +1410,7 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
         if (w16 && !swiglu && t128x48 * 10 >= ceil_div(t128x48, 3 * cus) * 3 * cus * 9)
             return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
         if (!swiglu && t128x64 * 10 >= ceil_div(t128x64, 2 * cus) * 2 * cus * 6) return "128x64x32_w2x2_sp4_pf3_il_dA";
+        if (rows64) return "64x64x64_w2x2_sp4_dAW";
     }
     if (rows128 && cols(192) && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
@@ -1602,6 +1603,20 @@ int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool sp
         const double fill128 = (double)t128 / (double)(ceil_div(t128, 2 * cus) * 2 * cus);
         const double fill96 = (double)t96 / (double)(ceil_div(t96, cus) * cus);
         if (t128 > 2 * cus && fill128 < 0.7 && fill96 >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
+    }
+    // the rule's 128 x 192 grid past one round of one workgroup per CU: the
+    // 32 x 96 tiles where their grid fills three quarters of its rounds
+    // (4096 x 4096 x 3072, two whole rounds: 745 against 782 us; 3072 x 1024
+    // x 3072, 384 tiles: 152.7 against 202.2; 4608 x 4096 x 1792, 360 tiles:
+    // 1.5x), else 64 x 64 tiles where it fills under 70% of its rounds
+    // (2304 x 1024 x 3072: 127.3 against 200.7); one whole round stays
+    // (1024 x 512 x 6144 with SwiGLU: 58.6 against 64.2 on 32 x 96)
+    if (op == kOpTN && same_name(f, "128x192x32_w2x2_sp8_pf4_il")) {
+        const int64_t t192 = ceil_div(M, 128) * ceil_div(N, 192), t96 = ceil_div(M, 32) * ceil_div(N, 96);
+        const double fill192 = (double)t192 / (double)(ceil_div(t192, cus) * cus);
+        const double fill96 = (double)t96 / (double)(ceil_div(t96, cus) * cus);
+        if (t192 > cus && fill96 >= 0.75) return bwd("32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4");
+        if (t192 > cus && fill192 < 0.7) return bwd("64x64x64_w2x2_sp4");
     }
     // a transposed B where the rule's 128 x 128 grid spans more than one
     // round of two workgroups per CU but fills under 70% of the rounds it
