@@ -100,6 +100,12 @@ def test_config_table(lib):
     assert pick(3072, 768, 1536, 1, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(2304, 768, 2304, 0, 1) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert pick(2304, 768, 2304, 1, 1) == "64x64x64_w2x2_sp4_dAW"
+    # a 64 x 64 grid filling under 70% of its rounds of two per CU
+    assert pick(1536, 768, 1536, 0, 1) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert pick(1536, 768, 1536, 1, 0) == "32x192x64_w1x4_sp4_pf3_il_dA_wr4"
+    assert pick(1536, 768, 1536, 1, 1) == "64x64x64_w2x2_sp4_dAW"
+    assert pick(2304, 768, 1152, 0, 1) == "128x48x32_w2x1_k2_sp4_pf3_il_dA"
+    assert pick(448, 768, 6528, 0, 1) == "64x64x64_w2x2_sp4_dAW"
     assert pick(8192, 768, 50304, 0, 1) == "128x128x32_w2x2_sp4_pf3_il_dA"
     # small grids with fp32 W keep W in registers; f16 W stages it through LDS
     assert pick(128, 768, 768, 0, 1) == "16x48x128_k4_sp4_dAW"

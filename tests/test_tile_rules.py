@@ -54,6 +54,14 @@ def _rows(M, seed, count=48, tail=128):
     (3072, 768, 1536, True, False, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
     (3001, 768, 1540, True, True, "64x64x64_w2x2_sp4_dAW"),
     (2304, 768, 2304, True, False, "128x64x32_w2x2_sp4_pf3_il_dA"),
+    # a 64 x 64 grid that fills under 70% of its rounds (576 tiles): 64 x 48
+    # where that grid fills whole rounds of three per CU, else 32 x 192 with
+    # fp32 W or 128 x 48 with f16 W where that grid fills its rounds
+    (1536, 768, 1536, False, False, "64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+    (1530, 768, 1532, True, True, "64x48x64_w2x1_k2_sp4_pf3_il_dA"),
+    (2304, 768, 1152, True, False, "128x48x32_w2x1_k2_sp4_pf3_il_dA"),
+    (2304, 768, 1152, False, False, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
+    (448, 768, 6528, True, False, "64x64x64_w2x2_sp4_dAW"),
     # one whole round of 64 x 64 tiles over a long contraction: K split in two
     (1024, 4096, 1024, False, False, "64x64x64_w2x2_sp4_ks2_dAW"),
     (1000, 4100, 1020, True, True, "64x64x64_w2x2_sp4_ks2_dAW"),
@@ -83,6 +91,7 @@ def test_forward_rule(M, K, N, w16, resid, tile):
     (384, 2048, 768, False, "16x96x128_w1x2_k2_sp8_pf2_il_wr4"),
     (8192, 3072, 32, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
     (3072, 768, 1536, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
+    (2300, 772, 1148, True, "32x192x64_w1x4_sp4_pf3_il_dA_wr4"),
     (8190, 3076, 36, True, "16x48x128_k4_sp4_pf3_il_dA_wr2"),
 ])
 def test_forward_rule_swiglu_fp32(M, K, N, ws, tile):

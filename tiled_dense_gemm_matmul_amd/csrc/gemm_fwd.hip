@@ -1414,7 +1414,26 @@ const char *select_rule(int64_t M, int64_t K, int64_t N, int swiglu, int w16, bo
     }
     if (rows128 && cols(192) && ceil_div(M, 128) * ceil_div(N, 192) >= cus) return "128x192x32_w2x2_sp8_pf4_il";
     const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64), t48 = ceil_div(M, 64) * ceil_div(N, 48);
-    if (rows64 && cols(64) && t64 >= 2 * cus) return "64x64x64_w2x2_sp4_dAW";
+    if (rows64 && cols(64) && t64 >= 2 * cus) {
+        // a forward 64 x 64 grid filling under 70% of its rounds of two per
+        // CU (576 tiles at 1536 x 768 x 1536: 39.5 us with fp32 W, 42.6 with
+        // f16 W, 49.1 with SwiGLU): 64 x 48 tiles without SwiGLU where their
+        // grid fills whole rounds of three per CU (33.5, 32.7), else fp32 W
+        // in registers on 32 x 192 tiles (37.0, 41.0 with SwiGLU) and f16 W
+        // without SwiGLU on 128 x 48 tiles where their grid fills three
+        // quarters of its rounds of two per CU (38.9 at 1536 x 768 x 1536,
+        // 39.0 against 42.2 at 2304 x 768 x 1152; 544 tiles at 448 x 768 x
+        // 6528 took 57.2 against 42.6); f16 W with SwiGLU stays
+        const int64_t t64x48 = ceil_div(M, 64) * ceil_div(N, 48);
+        if (forward && t64 * 10 < ceil_div(t64, 2 * cus) * 2 * cus * 7) {
+            if (!swiglu && t64x48 * 10 >= ceil_div(t64x48, 3 * cus) * 3 * cus * 9) return "64x48x64_w2x1_k2_sp4_pf3_il_dA";
+            if (!w16 && cols(192)) return "32x192x64_w1x4_sp4_pf3_il_dA_wr4";
+            const int64_t t128x48 = ceil_div(M, 128) * ceil_div(N, 48);
+            if (w16 && !swiglu && rows128 && t128x48 * 4 >= ceil_div(t128x48, 2 * cus) * 2 * cus * 3)
+                return "128x48x32_w2x1_k2_sp4_pf3_il_dA";
+        }
+        return "64x64x64_w2x2_sp4_dAW";
+    }
     if (rows64_round && cols(64) && forward && t48 >= cus && t48 < 2 * cus && t64 * 10 >= cus * 9 && t64 <= cus) {
         // over a contraction of 2048 or more with a workspace, K split in
         // two: two workgroups per CU instead of one (1024 x 4096 x 1024:
