@@ -429,6 +429,9 @@ def test_backward_selection(lib):
     assert name(1, 3072, 3072, 768) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 1536, 6144, 3072) == "128x64x32_w2x2_sp4_pf3_il_dA"
     assert name(1, 4096, 4096, 768) == "128x128x32_w2x2_sp4_pf3_il_dA"
+    # dX whose 128 x 64 or 64 x 64 grid fills under 60% of its rounds: 64 x 48
+    assert name(1, 512, 4352, 1536) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    assert name(1, 1024, 4352, 1536) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
     # dW whose 128 x 128 grid fills under 70% of its rounds: dY in registers
     assert name(2, 1024, 3072, 3072) == "32x96x128_w1x2_k2_sp4_pf3_il_dA_wr4"
     assert name(2, 1024, 4096, 4096) == "128x128x32_w2x2_sp4_pf3_il_dA"

@@ -219,6 +219,21 @@ def test_backward_matmul_t_partial_round(M, K, N):
     _cmp(dX.cpu().numpy()[rows], ref, scale, f"matmul_t {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(512, 4352, 1536), (1023, 4348, 1540)])
+def test_backward_matmul_t_partial_round_64x48(M, K, N):
+    # dX = dY @ W^T where the 64 x 64 (128 x 64) grid would fill under 60%
+    # of its rounds: 64 x 48
+    import torch
+    from tiled_dense_gemm_matmul_amd import binding
+    assert binding.bwd_kernel_config("matmul_t", M, K, N) == "64x48x64_w2x1_k2_sp4_pf3_il_dA"
+    c = inputs.backward_case(43 + K, M, K, N)
+    dX = binding.matmul_t(to_dev(c["dY"]), to_dev(c["W"]))
+    torch.cuda.synchronize()
+    rows = _rows(M, 19)
+    ref, scale = oracle.matmul_t(c["dY"], c["W"], rows=rows, want_scale=True)
+    _cmp(dX.cpu().numpy()[rows], ref, scale, f"matmul_t {M}x{K}x{N}")
+
+
 def test_backward_matmul_t_128x64():
     # dX = dY @ W^T for 8192 tokens, 768 outputs, 768 inputs
     import torch

@@ -1685,6 +1685,18 @@ int select_bwd_rule(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool sp
 // tokens, with or without a workspace: 159 -> 60 or 66 us.
 int select_bwd_config(int op, int64_t M, int64_t K, int64_t N, int swiglu, bool split) {
     const int r = select_bwd_rule(op, M, K, N, swiglu, split);
+    // a transposed B whose 128 x 64 or 64 x 64 grid spans more than one round
+    // of two workgroups per CU but fills under 60% of the rounds it takes:
+    // 64 x 48 tiles (512 x 1536 x 4352: 59.3 against 80.7 us on 64 x 64;
+    // 1024 x 1536 x 4352: 114.6 against 138.9 on 128 x 64; 2048 x 3072 x
+    // 2304: 223.2 against 274.4)
+    if (op == kOpNT && r >= 0 &&
+        (same_name(kBwdConfigs[r].name, "128x64x32_w2x2_sp4_pf3_il_dA") ||
+         same_name(kBwdConfigs[r].name, "64x64x64_w2x2_sp4"))) {
+        const int64_t t = ceil_div(M, kBwdConfigs[r].bm) * ceil_div(N, kBwdConfigs[r].bn);
+        if (t > 512 && t * 10 < ceil_div(t, 512) * 512 * 6)
+            return table_index(kBwdConfigs, kNumBwdConfigs, "64x48x64_w2x1_k2_sp4_pf3_il_dA");
+    }
     if (op != kOpNT || K < 2048 || r < 0) return r;
     const ConfigEntry &e = kBwdConfigs[r];
     const bool deep = same_name(e.name, "16x96x64_k4_sp8_pf3_il");
